@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Benchmark of the PARO W4A8 linear hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: the rotate-quant prologue followed by
+the W4A8 group GEMM, on the gate_up prefill workload (M=2048 tokens, K=5120, N=17408,
+synthetic seeded inputs, DRAM-fed: each step uses the next of `--copies` copies of the
+activations and weights so nothing stays resident in the 256 MB last-level cache).
+
+Prints ONE JSON line: whole-step TFLOP/s (2*M*N*K per step), the GEMM's roofline against
+the dense fp8 matrix peak (kernel time from HIP events on the launch stream), the decode
+M=1 / M=8 GEMM's HBM bandwidth against the 8 TB/s peak, and the oracle's CPU throughput on a
+bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A8 GEMM µs + TFLOP/s (gate_up M=2048), decode M=1 HBM GB/s vs peak"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 matrix peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PAGES_GEMM_TFLOPS = 125.5     # the pages' per-group fold v2 at this workload (gfx1201, context)
+
+
+def gemm_bytes(M, K, N, P=1):
+    G = K // 128
+    return K * N // 2 + G * N * 4 + P * M * K + 2 * P * M * G * 4 + M * N * 2
+
+
+def prologue_bytes(M, K, P=1):
+    G = K // 128
+    return M * K * 2 + P * K * 2 + P * 8 * (K // 2) * 8 + P * M * K + 2 * P * M * G * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=12)
+    ap.add_argument("--decode-reps", type=int, default=60)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); the multi-GPU path is design-only.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rotated_w4a8_group_amd as pq
+    import synth
+
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS["prefill"]
+    M, K, N, G, P = wl.M, wl.K, wl.N, wl.G, wl.P
+    C = max(1, args.copies)
+
+    # ---- inputs: C copies of activations and packed weights (DRAM-fed timing)
+    x0 = synth.activations(wl)
+    pl, tl, cl = synth.rotations(wl)
+    w = synth.weights(wl)
+    rec = torch.from_numpy(np.stack([pq.build_records(p, t) for p, t in zip(pl, tl)])).to(dev)
+    cs = torch.from_numpy(np.stack(cl)).to(dev)
+    xs = [torch.from_numpy(x0).to(dev)]
+    wq = [pq.pack_weights(torch.from_numpy(w.qweight).to(dev), torch.from_numpy(w.qzeros).to(dev),
+                          torch.from_numpy(w.scales).to(dev))]
+    for _ in range(C - 1):
+        xs.append(xs[0].clone())
+        wq.append((wq[0][0].clone(), wq[0][1].clone()))
+    A = torch.empty((P, M, K), dtype=torch.uint8, device=dev)
+    S = torch.empty((P, M, G), dtype=torch.float32, device=dev)
+    R = torch.empty((P, M, G), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        c = i % C
+        if ev is not None:
+            ev[0].record()
+        pq.rotate_quant(xs[c], rec, cs, out=(A, S, R))
+        if ev is not None:
+            ev[1].record()
+        pq.gemm(A, S, R, wq[c][0], wq[c][1], N, *wl.bounds, out=y)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    pro_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    flops = 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_GEMM_TFLOPS, 3),
+        "dtype": "fp8_e4m3 x u4 (fp32 accumulate)",
+        "data": "synthetic (seeded; shapes and distributions of the gate_up prefill workload)",
+        "config": {"workload": "gate_up prefill: rotate-quant prologue + W4A8 GEMM",
+                   "M": M, "K": K, "N": N, "partitions": P, "dram_fed_copies": C},
+        "gemm_us": round(gemm_ms * 1e3, 2),
+        "prologue_us": round(pro_ms * 1e3, 2),
+        "gemm_tflops": round(gemm_tflops, 2),
+        "prologue_gbs": round(prologue_bytes(M, K, P) / (pro_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "kernel": "gemm_prefill_kernel",
+                     "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None},
+    }
+
+    # ---- decode GEMM bandwidth (M = 1 and 8), DRAM-fed over the same weight copies
+    if not args.no_decode:
+        dec = {}
+        for Md in (1, 8):
+            Ad, Sd, Rd = A[:, :Md].contiguous(), S[:, :Md].contiguous(), R[:, :Md].contiguous()
+            yd = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)
+            for i in range(10):
+                pq.gemm(Ad, Sd, Rd, wq[i % C][0], wq[i % C][1], N, out=yd)
+            torch.cuda.synchronize()
+            e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.decode_reps)]
+            for i in range(args.decode_reps):
+                e[i][0].record()
+                pq.gemm(Ad, Sd, Rd, wq[i % C][0], wq[i % C][1], N, out=yd)
+                e[i][1].record()
+            torch.cuda.synchronize()
+            t = np.array([a.elapsed_time(b) for a, b in e]) * 1e-3
+            gbs = gemm_bytes(Md, K, N) / np.median(t) / 1e9
+            dec[f"M{Md}"] = {"us_median": round(float(np.median(t)) * 1e6, 2),
+                             "us_p10": round(float(np.percentile(t, 10)) * 1e6, 2),
+                             "us_p90": round(float(np.percentile(t, 90)) * 1e6, 2),
+                             "bytes": gemm_bytes(Md, K, N), "GBs": round(float(gbs), 1),
+                             "frac_hbm": round(float(gbs) / PEAK_HBM_GBS, 4)}
+        out["decode"] = dec
+
+    # ---- the oracle on the host, bounded sample of the same workload
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x0, pl, tl, cl, w, wl)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(x0, pl, tl, cl, w, wl):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import gemm as ogemm
+    from oracle import prologue as opro
+
+    rows = np.arange(wl.M)
+    t0 = time.perf_counter()
+    A, S, _ = opro.rotate_quant(x0[rows], pl, tl, cl)
+    ogemm.gemm_ref(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * wl.N * wl.K
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {wl.M} token rows, all {wl.N} columns, prologue + GEMM "
+                      f"({dt:.1f} s wall; BLAS threads for the per-group fp64 products)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,145 @@
+/*
+ * pq.h — C ABI of the PARO W4A8 linear hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one on the page "ParoQuant (PARO) W4A8 on gfx1201 — engineering log"
+ * (sections "Format" and "Design"): activations are channel-scaled and rotated through 8
+ * layers of pairwise Givens rotations local to each 128-channel group, quantised per
+ * (token, group) to OCP e4m3 with code-domain row-sums (the prologue), then multiplied by
+ * AWQ-packed uint4 asymmetric group-128 weights whose zero point enters as a row-sum
+ * correction (the GEMM). Merged linears carry up to 3 activation partitions.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_d are device pointers, *_h host pointers. The caller allocates every
+ *    buffer and keeps it alive until the stream has passed the call; the library allocates
+ *    nothing and keeps no pointer after returning.
+ *  - Work is queued on `stream` (a hipStream_t; NULL = the default stream). Nothing
+ *    synchronises. Asynchronous device faults surface at the caller's next synchronisation.
+ *  - Every argument is validated before anything is launched. On error nothing is launched,
+ *    no output is touched, a negative PQ_ERR_* code is returned and pq_last_error() holds a
+ *    message (per calling thread). M == 0 is a valid no-op.
+ *  - Element types: f16 and bf16 are passed as uint16_t bit patterns.
+ *  - No environment variables are read and nothing is printed.
+ */
+#ifndef PQ_H_
+#define PQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PQ_ABI_VERSION 1
+#define PQ_GROUP 128
+#define PQ_LAYERS 8
+#define PQ_MAX_PARTITIONS 3
+/* "no boundary" value for pb1 / pb2 */
+#define PQ_NO_BOUNDARY 0x7FFFFFFF
+
+typedef struct ihipStream_t* pq_stream_t; /* same type as hipStream_t */
+
+enum pq_status {
+  PQ_OK = 0,
+  PQ_ERR_NULL = -1,      /* a required pointer is NULL */
+  PQ_ERR_SHAPE = -2,     /* a size or stride is out of range */
+  PQ_ERR_ALIGN = -3,     /* a pointer or stride is not aligned as required */
+  PQ_ERR_PARTITION = -4, /* P or the partition boundaries are inconsistent */
+  PQ_ERR_RECORDS = -5,   /* a 128-slice of `pairs` is not a permutation of 0..127 */
+  PQ_ERR_WORKSPACE = -6, /* workspace smaller than pq_gemm_workspace_bytes() */
+  PQ_ERR_DEVICE = -7     /* the HIP runtime reported an error at launch */
+};
+
+/* ABI version of the loaded library (PQ_ABI_VERSION it was built with). */
+int pq_abi_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* pq_last_error(void);
+
+/*
+ * Rotation records (host only, load time).
+ *
+ * pairs_h  int16 [8, K]: per layer, every 128-slice is a permutation of 0..127; pair q of
+ *          layer r is (pairs[r, 2q], pairs[r, 2q+1]), channels local to group q/64.
+ * theta_h  f16 [8, K/2]: the angle of pair q of layer r.
+ * rec_h    out, 8 * (K/2) records of 8 bytes, layout [8][K/2]: {uint32 i | j << 8,
+ *          f16 cos, f16 sin} with cos/sin = f16 round-to-nearest-even of the fp64 cos/sin of
+ *          the f16 angle. Within each (layer, group) the 64 records are stored in the order
+ *          the prologue's 64 lanes consume them, and a record may list its pair as (j, i) with
+ *          sin negated (the same rotation). For P partitions call once per partition and
+ *          concatenate: [P][8][K/2].
+ * Source: section "Format" (pairs/theta) and "Design" item 3 (8-byte records).
+ * Errors: PQ_ERR_NULL, PQ_ERR_SHAPE (K <= 0 or K % 128), PQ_ERR_RECORDS.
+ */
+int pq_build_records(const int16_t* pairs_h, const uint16_t* theta_h, int K, void* rec_h);
+
+/*
+ * Weight packing (device, load time): AWQ tensors -> the GEMM's operands.
+ *
+ * qweight_d int32 [K, N/8], qzeros_d int32 [K/128, N/8]: AWQ words, nibble i of word j holds
+ *           column 8j + (0,2,4,6,1,3,5,7)[i]; zero points stored as-is (section "Format").
+ * scales_d  f16 [K/128, N].
+ * wpk_d     out, K*N/2 bytes (pq_packed_weight_bytes): the same 4-bit codes reordered into
+ *           matrix-core fragment order, 1 KiB per (16 columns, 128-group).
+ * sz_d      out, f16 [K/128, N, 2]: {sc, fl16(sc * (zp - 8))} interleaved ("Design" item 1).
+ * Requires K % 128 == 0, N % 16 == 0, 16-byte aligned wpk_d, 4-byte aligned others.
+ */
+size_t pq_packed_weight_bytes(int K, int N);
+int pq_pack_weights(const int32_t* qweight_d, const int32_t* qzeros_d, const uint16_t* scales_d,
+                    int K, int N, void* wpk_d, uint16_t* sz_d, pq_stream_t stream);
+
+/*
+ * Rotate-quant prologue (device): per partition p, token m, group g —
+ *   v = x * cs_p; 8 Givens layers (a, b) -> (c*a + s*b, c*b - s*a) in fp32 without fused
+ *   multiply-add; amax = max|v|; asg = amax * fl32(1/448); codes = e4m3(v * fl32(1/asg))
+ *   (OCP E4M3FN, round to nearest even, NaN -> 0, -0 -> +0, clamped to +-448);
+ *   rs = fl32(exact sum of the decoded codes). An all-zero group gives codes 0, asg 0, rs 0.
+ * Source: "Format" (inference identity), "Design" items 2-3, "Gates passed" (amax*(1/448.f)).
+ *
+ * x_d    f16 [M, ldx] (first K columns used), 4-byte aligned, ldx even and >= K.
+ * rec_d  [P][8][K/2] records from pq_build_records, 8-byte aligned.
+ * cs_d   f16 [P, K] pre-inverted channel scales (multiply), 4-byte aligned.
+ * a_d    out u8 [P, M, K] e4m3 codes, 16-byte aligned.
+ * asg_d  out f32 [P, M, K/128] group scales; rs_d out f32 [P, M, K/128] code-domain sums.
+ * 1 <= P <= 3, K % 128 == 0.
+ */
+int pq_rotate_quant(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const void* rec_d,
+                    const uint16_t* cs_d, uint8_t* a_d, float* asg_d, float* rs_d,
+                    pq_stream_t stream);
+
+/*
+ * W4A8 group GEMM (device): for column n in partition p(n) = [n >= pb1] + [n >= pb2],
+ *   y[m, n] = bf16_rne( sum_g asg_p[m,g] * ( sc[g,n] * sum_{k in g} D(A_p[m,k]) * (c[k,n] - 8)
+ *                                            - fl16(sc[g,n]*(zp[g,n]-8)) * rs_p[m,g] ) )
+ * i.e. the zero point enters as a row-sum correction ("Design" item 1), one launch for all
+ * partitions ("Design" item 4). Rows m >= M of y are never written.
+ *
+ * a_d/asg_d/rs_d  prologue outputs for P partitions (layouts above), a_d 16-byte aligned.
+ * wpk_d, sz_d     from pq_pack_weights for this K, N.
+ * pb1, pb2        partition boundaries: PQ_NO_BOUNDARY (or >= N) when unused; finite ones
+ *                 satisfy 0 < pb1 < pb2 < N and are multiples of 128; P must equal
+ *                 1 + the number of boundaries below N.
+ * y_d             out bf16 [M, ldy], ldy >= N, 4-byte aligned, ldy even.
+ * ws_d, ws_bytes  workspace of at least pq_gemm_workspace_bytes(M, N, K) bytes (may be NULL
+ *                 when that is 0).
+ * Requires K % 128 == 0, N % 16 == 0.
+ */
+size_t pq_gemm_workspace_bytes(int M, int N, int K);
+int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
+            const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+            int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream);
+
+/*
+ * Verification hooks: run the exact device arithmetic the prologue uses on plain arrays, so
+ * tests can check it exhaustively.
+ *  pq_e4m3_encode: codes_d[i] = E(q_d[i]) with the prologue's encoder (n >= 0).
+ *  pq_recip_f32:   y_d[i] = 1 / x_d[i] with the prologue's reciprocal.
+ */
+int pq_e4m3_encode(const float* q_d, uint8_t* codes_d, int64_t n, pq_stream_t stream);
+int pq_recip_f32(const float* x_d, float* y_d, int64_t n, pq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQ_H_ */

@@ -1,0 +1,189 @@
+"""PARO W4A8 linear hot path on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/pq.h`` (``libpq.so`` in this directory).
+It only marshals arguments: every step of the path runs in the library's HIP kernels.
+PyTorch supplies device memory and the current HIP stream. There is no fallback: if the
+library is missing or fails to load, every call raises.
+
+Calls (same names as the C entry points, without the ``pq_`` prefix):
+
+* ``build_records(pairs, theta)``            host; numpy int16 [8, K], f16 [8, K/2]
+* ``pack_weights(qweight, qzeros, scales)``  device; AWQ tensors -> (wpk, sz)
+* ``rotate_quant(x, rec, cs)``               device; -> (A, ASG, RS)
+* ``gemm(A, ASG, RS, wpk, sz, N, pb1, pb2)`` device; -> y bf16
+* ``e4m3_encode(q)``, ``recip_f32(x)``       device verification hooks
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpq.so")
+
+GROUP = 128
+LAYERS = 8
+NO_BOUNDARY = 0x7FFFFFFF
+
+PQ_OK = 0
+ERRORS = {
+    -1: "PQ_ERR_NULL", -2: "PQ_ERR_SHAPE", -3: "PQ_ERR_ALIGN", -4: "PQ_ERR_PARTITION",
+    -5: "PQ_ERR_RECORDS", -6: "PQ_ERR_WORKSPACE", -7: "PQ_ERR_DEVICE",
+}
+
+# name -> (restype, argtypes); keep in step with include/pq.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "pq_abi_version": (_I, []),
+    "pq_last_error": (ctypes.c_char_p, []),
+    "pq_build_records": (_I, [_P, _P, _I, _P]),
+    "pq_packed_weight_bytes": (_SZ, [_I, _I]),
+    "pq_pack_weights": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
+    "pq_rotate_quant": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "pq_gemm_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "pq_gemm": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
+    "pq_e4m3_encode": (_I, [_P, _P, _I64, _P]),
+    "pq_recip_f32": (_I, [_P, _P, _I64, _P]),
+}
+
+
+class PQError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn}: {ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (loaded once). Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m rotated_w4a8_group_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, code):
+    if code != PQ_OK:
+        raise PQError(fn, code, lib().pq_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name}: expected a contiguous CUDA tensor of {dtype}")
+
+
+# ------------------------------------------------------------------------------------------
+def build_records(pairs, theta):
+    """pairs int16 [8, K], theta f16 [8, K/2] (numpy, host) -> uint8 [8, K/2, 8] records."""
+    pairs = np.ascontiguousarray(pairs, dtype=np.int16)
+    theta = np.ascontiguousarray(theta, dtype=np.float16)
+    K = pairs.shape[1]
+    out = np.zeros((LAYERS, K // 2, 8), dtype=np.uint8)
+    _check("pq_build_records", lib().pq_build_records(
+        pairs.ctypes.data_as(_P), theta.view(np.uint16).ctypes.data_as(_P), K, out.ctypes.data_as(_P)))
+    return out
+
+
+def pack_weights(qweight, qzeros, scales, stream=None):
+    """AWQ qweight int32 [K, N/8], qzeros int32 [K/128, N/8], scales f16 [K/128, N] (CUDA)
+    -> (wpk uint8 [K*N/2], sz f16 [K/128, N, 2])."""
+    import torch
+    _need(qweight, torch.int32, "qweight")
+    _need(qzeros, torch.int32, "qzeros")
+    _need(scales, torch.float16, "scales")
+    K, N = qweight.shape[0], qweight.shape[1] * 8
+    wpk = torch.empty(lib().pq_packed_weight_bytes(K, N), dtype=torch.uint8, device=qweight.device)
+    sz = torch.empty((K // GROUP, N, 2), dtype=torch.float16, device=qweight.device)
+    _check("pq_pack_weights", lib().pq_pack_weights(
+        _ptr(qweight), _ptr(qzeros), _ptr(scales), K, N, _ptr(wpk), _ptr(sz), _stream(stream)))
+    return wpk, sz
+
+
+def rotate_quant(x, rec, cs, out=None, stream=None):
+    """x f16 [M, K] (row stride may exceed K), rec uint8 [P, 8, K/2, 8] (or [8, K/2, 8]),
+    cs f16 [P, K] -> (A u8 [P, M, K], ASG f32 [P, M, G], RS f32 [P, M, G])."""
+    import torch
+    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise TypeError("x: expected a CUDA float16 [M, K] tensor with unit column stride")
+    _need(rec, torch.uint8, "rec")
+    _need(cs, torch.float16, "cs")
+    M, K = x.shape
+    P = cs.shape[0] if cs.dim() == 2 else 1
+    G = K // GROUP
+    if out is None:
+        A = torch.empty((P, M, K), dtype=torch.uint8, device=x.device)
+        ASG = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
+        RS = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
+    else:
+        A, ASG, RS = out
+    _check("pq_rotate_quant", lib().pq_rotate_quant(
+        _ptr(x), x.stride(0), M, K, P, _ptr(rec), _ptr(cs), _ptr(A), _ptr(ASG), _ptr(RS), _stream(stream)))
+    return A, ASG, RS
+
+
+def gemm_workspace_bytes(M, N, K):
+    return int(lib().pq_gemm_workspace_bytes(M, N, K))
+
+
+def gemm(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, workspace=None, stream=None):
+    """A u8 [P, M, K], ASG/RS f32 [P, M, G], packed weights -> y bf16 [M, N] (or into ``out``,
+    a bf16 [M, ldy] view with unit column stride)."""
+    import torch
+    _need(A, torch.uint8, "A")
+    _need(ASG, torch.float32, "ASG")
+    _need(RS, torch.float32, "RS")
+    _need(wpk, torch.uint8, "wpk")
+    _need(sz, torch.float16, "sz")
+    P, M, K = A.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
+        raise TypeError("out: expected a bf16 [M, ldy] tensor with unit column stride")
+    ws_bytes = gemm_workspace_bytes(M, N, K)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
+    _check("pq_gemm", lib().pq_gemm(
+        _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2,
+        _ptr(out), out.stride(0), _ptr(workspace), ws_bytes if workspace is not None else 0, _stream(stream)))
+    return out
+
+
+def e4m3_encode(q, stream=None):
+    """float32 CUDA tensor -> uint8 codes with the prologue's device encoder."""
+    import torch
+    _need(q, torch.float32, "q")
+    out = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    _check("pq_e4m3_encode", lib().pq_e4m3_encode(_ptr(q), _ptr(out), q.numel(), _stream(stream)))
+    return out
+
+
+def recip_f32(x, stream=None):
+    """float32 CUDA tensor -> 1/x with the prologue's device reciprocal."""
+    import torch
+    _need(x, torch.float32, "x")
+    out = torch.empty_like(x)
+    _check("pq_recip_f32", lib().pq_recip_f32(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    return out

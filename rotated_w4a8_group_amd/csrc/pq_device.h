@@ -1,0 +1,43 @@
+// Device helpers shared by the library's kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace pq {
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu)));
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// OCP E4M3FN encode of two floats into the low 16 bits (first value in the low byte):
+// NaN -> 0, -0 -> +0, clamp to +-448, then the hardware round-to-nearest-even convert.
+// The hardware convert alone does not saturate (it yields NaN above 464) and keeps -0 and NaN;
+// this wrapper is the encoder of "ParoQuant (PARO) W4A8 on gfx1201 — engineering log",
+// section "hardware e4m3 convert in the producers".
+__device__ __forceinline__ float e4m3_prep(float q) {
+  q = (q == q) ? q : 0.0f;                                   // NaN -> 0
+  q = __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f);  // saturate
+  return (__builtin_bit_cast(uint32_t, q) == 0x80000000u) ? 0.0f : q;  // -0 -> +0
+}
+
+__device__ __forceinline__ uint32_t e4m3_encode2(float q0, float q1) {
+  return static_cast<uint32_t>(
+             __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(q0), e4m3_prep(q1), 0, false)) & 0xFFFFu;
+}
+
+// 512 * D(code) as an integer (exact: every finite E4M3FN value is a multiple of 2^-9).
+__device__ __forceinline__ int e4m3_units(uint32_t code) {
+  const int e = (code >> 3) & 15, m = code & 7;
+  const int mag = (e == 0) ? m : ((8 + m) << (e - 1));
+  return (code & 0x80u) ? -mag : mag;
+}
+
+}  // namespace pq

@@ -1,0 +1,161 @@
+"""CPU-side tests of the C-ABI library: it loads, exports every symbol include/pq.h declares,
+its host-only record builder agrees with the oracle, and every validation path returns the
+documented error before anything is launched (no GPU is touched here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rotated_w4a8_group_amd as pq
+import synth
+from oracle import records as orec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = pq.lib()
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(pq.SIGNATURES), "binding signatures out of step with include/pq.h"
+
+
+def test_abi_version():
+    m = re.search(r"#define PQ_ABI_VERSION (\d+)", open(HEADER).read())
+    assert pq.lib().pq_abi_version() == int(m.group(1))
+
+
+def _canon(i, j, c16, s16):
+    """A pair listed as (j, i) with sin negated is the same rotation."""
+    if i < j:
+        return (int(i), int(j), int(c16), int(s16))
+    return (int(j), int(i), int(c16), int(s16) ^ 0x8000)
+
+
+@pytest.mark.parametrize("wl_name", ["tiny", "qkv"])
+def test_records_match_oracle_up_to_lane_order(wl_name):
+    wl = synth.WORKLOADS[wl_name]
+    pl, tl, _ = synth.rotations(wl)
+    for pairs, theta in zip(pl, tl):
+        if wl.K > 1024:
+            pairs, theta = pairs[:, :1024], theta[:, :512]
+        lib = pq.build_records(pairs, theta)          # [8, K/2, 8]
+        ref = orec.build(pairs, theta)
+        ij = lib[..., :4].copy().view(np.uint32)[..., 0]
+        li, lj = ij & 0xFF, (ij >> 8) & 0xFF
+        lc = lib[..., 4:6].copy().view(np.uint16)[..., 0]
+        ls = lib[..., 6:8].copy().view(np.uint16)[..., 0]
+        K = pairs.shape[1]
+        for r in range(8):
+            for g in range(K // 128):
+                sl = slice(64 * g, 64 * g + 64)
+                a = sorted(_canon(*t) for t in zip(li[r, sl], lj[r, sl], lc[r, sl], ls[r, sl]))
+                b = sorted(_canon(*t) for t in zip(ref["i"][r, sl], ref["j"][r, sl],
+                                                   ref["cos16"][r, sl], ref["sin16"][r, sl]))
+                assert a == b, (r, g)
+
+
+def test_records_lane_order_is_bank_conflict_free():
+    wl = synth.WORKLOADS["qkv"]
+    pl, tl, _ = synth.rotations(wl)
+    lib = pq.build_records(pl[1][:, :2048], tl[1][:, :1024])
+    ij = lib[..., :4].copy().view(np.uint32)[..., 0]
+    for r in range(8):
+        for g in range(16):
+            t = (ij[r, 64 * g:64 * g + 64] & 0xFF).astype(int)
+            h = ((ij[r, 64 * g:64 * g + 64] >> 8) & 0xFF).astype(int)
+            assert len(set(t % 64)) == 64 and len(set(h % 64)) == 64
+            for half in (slice(0, 32), slice(32, 64)):
+                assert len(set(t[half] % 32)) == 32 and len(set(h[half] % 32)) == 32
+
+
+def test_records_reject_bad_pairs():
+    pairs = np.tile(np.arange(128, dtype=np.int16), (8, 2))
+    theta = np.zeros((8, 128), np.float16)
+    pairs[5, 130] = pairs[5, 131]
+    with pytest.raises(pq.PQError) as e:
+        pq.build_records(pairs, theta)
+    assert e.value.code == -5
+    with pytest.raises(pq.PQError) as e:
+        pq.lib().pq_build_records(None, None, 256, None) and None
+        pq._check("pq_build_records", pq.lib().pq_build_records(None, None, 256, None))
+    assert e.value.code == -1
+
+
+FAKE = ctypes.c_void_p(0x100000)   # aligned, never dereferenced: validation fails first or M == 0
+
+
+def _gemm(**kw):
+    a = dict(a=FAKE, asg=FAKE, rs=FAKE, M=4, K=256, P=1, wpk=FAKE, sz=FAKE, N=128,
+             pb1=pq.NO_BOUNDARY, pb2=pq.NO_BOUNDARY, y=FAKE, ldy=128, ws=None, ws_bytes=0, s=None)
+    a.update(kw)
+    return pq.lib().pq_gemm(a["a"], a["asg"], a["rs"], a["M"], a["K"], a["P"], a["wpk"], a["sz"],
+                            a["N"], a["pb1"], a["pb2"], a["y"], a["ldy"], a["ws"], a["ws_bytes"], a["s"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=100), -2), (dict(K=0), -2), (dict(N=120), -2), (dict(M=-1), -2), (dict(ldy=64), -2),
+    (dict(ldy=129), -2), (dict(P=0), -4), (dict(P=4), -4), (dict(P=2), -4),
+    (dict(P=2, pb1=64), -4), (dict(P=2, pb1=0), -4), (dict(P=3, pb1=256, pb2=128, N=512, ldy=512), -4),
+    (dict(P=1, pb1=128, N=256, ldy=256), -4),
+    (dict(P=2, pb1=pq.NO_BOUNDARY, pb2=128, N=256, ldy=256), -4),
+    (dict(a=None), -1), (dict(y=None), -1), (dict(a=ctypes.c_void_p(0x100004)), -3),
+    (dict(y=ctypes.c_void_p(0x100002)), -3),
+])
+def test_gemm_validation(kw, code):
+    assert _gemm(**kw) == code
+    assert pq.lib().pq_last_error().decode()
+
+
+def test_gemm_m0_is_noop_and_partition_ok():
+    assert _gemm(M=0, a=None, y=None) == 0
+    assert _gemm(M=0, P=3, N=8192, pb1=6144, pb2=7168, ldy=8192) == 0
+    assert _gemm(M=0, P=2, N=256, pb1=128, ldy=256) == 0
+    assert pq.gemm_workspace_bytes(8, 17408, 5120) == 0
+
+
+def _rq(**kw):
+    a = dict(x=FAKE, ldx=256, M=4, K=256, P=1, rec=FAKE, cs=FAKE, A=FAKE, asg=FAKE, rs=FAKE, s=None)
+    a.update(kw)
+    return pq.lib().pq_rotate_quant(a["x"], a["ldx"], a["M"], a["K"], a["P"], a["rec"], a["cs"],
+                                    a["A"], a["asg"], a["rs"], a["s"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=200), -2), (dict(M=-2), -2), (dict(ldx=255), -2), (dict(ldx=128), -2), (dict(P=4), -4),
+    (dict(P=0), -4), (dict(x=None), -1), (dict(rs=None), -1), (dict(A=ctypes.c_void_p(0x100008)), -3),
+    (dict(x=ctypes.c_void_p(0x100002)), -3), (dict(rec=ctypes.c_void_p(0x100004)), -3),
+])
+def test_rotate_quant_validation(kw, code):
+    assert _rq(**kw) == code
+
+
+def test_rotate_quant_m0_noop():
+    assert _rq(M=0, x=None, A=None) == 0
+
+
+def test_pack_validation():
+    L = pq.lib()
+    assert L.pq_pack_weights(FAKE, FAKE, FAKE, 100, 128, FAKE, FAKE, None) == -2
+    assert L.pq_pack_weights(FAKE, FAKE, FAKE, 256, 8, FAKE, FAKE, None) == -2
+    assert L.pq_pack_weights(None, FAKE, FAKE, 256, 128, FAKE, FAKE, None) == -1
+    assert L.pq_pack_weights(FAKE, FAKE, FAKE, 256, 128, ctypes.c_void_p(0x100008), FAKE, None) == -3
+    assert L.pq_packed_weight_bytes(5120, 17408) == 5120 * 17408 // 2
+
+
+def test_hooks_validation():
+    L = pq.lib()
+    assert L.pq_e4m3_encode(FAKE, FAKE, -1, None) == -2
+    assert L.pq_e4m3_encode(None, None, 0, None) == 0
+    assert L.pq_recip_f32(None, FAKE, 5, None) == -1
