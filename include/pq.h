@@ -79,8 +79,11 @@ int pq_build_records(const int16_t* pairs_h, const uint16_t* theta_h, int K, voi
  * qweight_d int32 [K, N/8], qzeros_d int32 [K/128, N/8]: AWQ words, nibble i of word j holds
  *           column 8j + (0,2,4,6,1,3,5,7)[i]; zero points stored as-is (section "Format").
  * scales_d  f16 [K/128, N].
- * wpk_d     out, K*N/2 bytes (pq_packed_weight_bytes): the same 4-bit codes reordered into
- *           matrix-core fragment order, 1 KiB per (16 columns, 128-group).
+ * wpk_d     out, pq_packed_weight_bytes(K, N) bytes: first K*N/2 bytes hold the same 4-bit
+ *           codes reordered into matrix-core fragment order (1 KiB per 16 columns x 128-group);
+ *           then, per 16 columns, ceil(3*(K/128)/32) KiB of bf16 operands for the zero-point
+ *           epilogue (the f32 values 8*sc + fl16(sc*(zp-8)) split into two bf16 pieces).
+ *           Returns 0 for shapes the library rejects.
  * sz_d      out, f16 [K/128, N, 2]: {sc, fl16(sc * (zp - 8))} interleaved ("Design" item 1).
  * Requires K % 128 == 0, N % 16 == 0, 16-byte aligned wpk_d, 4-byte aligned others.
  */
@@ -120,8 +123,10 @@ int pq_rotate_quant(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const
  *                 satisfy 0 < pb1 < pb2 < N and are multiples of 128; P must equal
  *                 1 + the number of boundaries below N.
  * y_d             out bf16 [M, ldy], ldy >= N, 4-byte aligned, ldy even.
- * ws_d, ws_bytes  workspace of at least pq_gemm_workspace_bytes(M, N, K) bytes (may be NULL
- *                 when that is 0).
+ * ws_d, ws_bytes  device workspace of at least pq_gemm_workspace_bytes(M, N, K) bytes, 16-byte
+ *                 aligned (may be NULL when that is 0: M <= 16). For M > 16 the call first
+ *                 writes the activation operand of the zero-point epilogue there (sized for up
+ *                 to 3 partitions); its contents need no initialisation and are not kept.
  * Requires K % 128 == 0, N % 16 == 0.
  */
 size_t pq_gemm_workspace_bytes(int M, int N, int K);

@@ -26,7 +26,8 @@ SOURCES = [
     ("pq_host.cpp", []),
     # the prologue's results are defined by binary32 ops that each round: no contraction
     ("pq_prologue.hip", ["-ffp-contract=off"]),
-    ("pq_gemm.hip", []),
+    # matrix-core results land in VGPRs (the fold reads them there; no AGPR copies)
+    ("pq_gemm.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
 ]
 
 

@@ -27,6 +27,7 @@ namespace pq {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -99,15 +100,92 @@ __global__ void pack_sz_kernel(const int32_t* __restrict__ qzeros, const uint16_
 }
 
 // ---------------------------------------------------------------------------------------
-// decode: M <= 16. One workgroup per 16*NT columns; its WV waves split the groups and their
-// partial sums meet in LDS. Each wave streams NT x 1 KiB of packed weights per group.
+// zero-point epilogue operand (load time). The prefill kernel moves the zero-point term
+//   Z[m, n] = sum_g (asg * rs)[m, g] * (8 sc + zsc)[g, n]
+// out of its group loop ("zero-point epilogue" of the page) and computes it once per tile as
+// a bf16 matrix-core product with split operands: ar = a1 + a2 and zz = z1 + z2 (each piece the
+// bf16 rounding of what is left), Z ~= a1 z1 + a1 z2 + a2 z1 (relative error ~2^-16).
+// K' = 3G is laid out as [a1 | a1 | a2] x [z1 ; z2 ; z1], padded with zeros to whole chunks of 32.
+// Layout per 16-column tile t and chunk c: 1 KiB, lane l (column 16t + l%16) holds the 8 bf16
+// at k' = 32c + 8(l/16) + 0..7 — the bf16 16x16x32 B operand.
+__host__ __device__ constexpr int zpe_chunks(int G) { return (3 * G + 31) / 32; }
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, (h & 0xFFFFu) << 16); }
+
+__global__ void pack_zpe_kernel(const uint32_t* __restrict__ sz, int G, int N, u32x4* __restrict__ zpe) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int KC = zpe_chunks(G);
+  if (idx >= static_cast<int64_t>(N / 16) * KC * 64) return;
+  const int l = static_cast<int>(idx & 63);
+  const int c = static_cast<int>((idx >> 6) % KC);
+  const int t = static_cast<int>((idx >> 6) / KC);
+  const int n = 16 * t + (l & 15);
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int kp = 32 * c + 8 * (l >> 4) + e;
+    uint32_t v = 0;
+    if (kp < 3 * G) {
+      const int piece = kp / G, g = kp % G;
+      const float2 f = sz_factors(sz[static_cast<size_t>(g) * N + n]);
+      const uint32_t z1 = f32_to_bf16(f.y);
+      v = (piece == 1) ? f32_to_bf16(f.y - bf16_to_f32(z1)) : z1;
+    }
+    h[e] = v;
+  }
+  zpe[idx] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
+
+// Activation side of the zero-point epilogue, built per GEMM call into the workspace:
+// for partition p, 16-row tile mt and chunk c, 1 KiB where lane l (row 16mt + l%16) holds the
+// 8 bf16 at k' = 32c + 8(l/16) + 0..7 of -[a1 | a1 | a2], ar = asg * rs = a1 + a2 (bf16 pieces).
+__global__ void zpe_act_kernel(const float* __restrict__ ASG, const float* __restrict__ RS, int M, int G,
+                               int P, u32x4* __restrict__ zpa) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int KC = zpe_chunks(G), MT = (M + 15) / 16;
+  if (idx >= static_cast<int64_t>(P) * MT * KC * 64) return;
+  const int l = static_cast<int>(idx & 63);
+  int64_t rest = idx >> 6;
+  const int c = static_cast<int>(rest % KC);
+  rest /= KC;
+  const int mt = static_cast<int>(rest % MT);
+  const int p = static_cast<int>(rest / MT);
+  const int row = 16 * mt + (l & 15);
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int kp = 32 * c + 8 * (l >> 4) + e;
+    uint32_t v = 0;
+    if (kp < 3 * G && row < M) {
+      const int piece = kp / G, g = kp % G;
+      const size_t o = (static_cast<size_t>(p) * M + row) * G + g;
+      const float ar = ASG[o] * RS[o];
+      const uint32_t a1 = f32_to_bf16(ar);
+      v = ((piece == 2) ? f32_to_bf16(ar - bf16_to_f32(a1)) : a1) ^ 0x8000u;   // negated
+    }
+    h[e] = v;
+  }
+  zpa[idx] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
+
+size_t zpe_act_bytes(int M, int G, int P) {
+  return static_cast<size_t>(P) * ((M + 15) / 16) * zpe_chunks(G) * 1024;
+}
+
+// ---------------------------------------------------------------------------------------
+// decode: M <= 16. One workgroup per 16*NT columns; its WV waves split the groups (partial sums
+// meet in LDS). Each wave runs a 3-slot register ring over its groups: the loads of group g+2
+// (weights, activation fragment, SZ words) are issued before group g is computed, so two
+// groups are always in flight and no load waits on another. The per-(row, group) scales are
+// staged in LDS once per workgroup with all their loads issued together.
 template <int NT, int WV>
-__global__ __launch_bounds__(64 * WV) void gemm_decode_kernel(
+__global__ __launch_bounds__(64 * WV, (WV == 4 ? 3 : 4)) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ ASG, const float* __restrict__ RS,
     int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ sz, int N,
     int pb1, int pb2, uint16_t* __restrict__ y, int64_t ldy) {
+  extern __shared__ __attribute__((aligned(16))) float dsm[];   // [M*G] asg, [M*G] rs; later the reduction
   const int G = K >> 7;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, kq = lane >> 4;
   const int n0 = blockIdx.x * (16 * NT);
   const int p = (n0 >= pb1) + (n0 >= pb2);
@@ -115,128 +193,344 @@ __global__ __launch_bounds__(64 * WV) void gemm_decode_kernel(
 
   const bool arow = col < M;  // A operand row = lane % 16
   const uint8_t* Ap = A + (static_cast<size_t>(p) * M + (arow ? col : 0)) * K + 32 * kq;
+  const u32x4* wp = wpk + static_cast<size_t>(n0 / 16) * G * 64 + lane;
+  const uint32_t* szp = sz + n0 + col;
+
+  u32x4 bw[3][NT];
+  uint32_t zw[3][NT];
+  v8i av[3];
+  auto issue = [&](int slot, int g) {
+    if (g < g1) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) bw[slot][t] = __builtin_nontemporal_load(wp + (static_cast<size_t>(t) * G + g) * 64);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) zw[slot][t] = szp[static_cast<size_t>(g) * N + 16 * t];
+      av[slot] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      if (arow) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(Ap + 128 * g);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(Ap + 128 * g + 16);
+        av[slot] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      }
+    }
+  };
+  issue(0, g0);
+  issue(1, g0 + 1);
+
+  float* s_as = dsm;
+  float* s_rs = dsm + M * G;
   const float* asgp = ASG + static_cast<size_t>(p) * M * G;
   const float* rsp = RS + static_cast<size_t>(p) * M * G;
-  const u32x4* wp = wpk + static_cast<size_t>(n0 / 16) * G * 64 + lane;
+  for (int i0 = 0; i0 < M * G; i0 += 4 * 64 * WV) {
+    float va[4], vr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 64 * WV + tid;
+      va[u] = (i < M * G) ? asgp[i] : 0.f;
+      vr[u] = (i < M * G) ? rsp[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 64 * WV + tid;
+      if (i < M * G) { s_as[i] = va[u]; s_rs[i] = vr[u]; }
+    }
+  }
+  __syncthreads();
 
   v4f acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int g = g0; g < g1; ++g) {
-    u32x4 bw[NT];
+  for (int gb = g0; gb < g1; gb += 3) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) bw[t] = __builtin_nontemporal_load(wp + (static_cast<size_t>(t) * G + g) * 64);
-    v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (arow) {
-      const uint4 a0 = *reinterpret_cast<const uint4*>(Ap + 128 * g);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(Ap + 128 * g + 16);
-      a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-    }
-    float as[4], rs[4];
+    for (int sl = 0; sl < 3; ++sl) {
+      const int g = gb + sl;
+      if (g < g1) {
+        issue((sl + 2) % 3, g + 2);
+        float as[4], rs[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * kq + i;
-      as[i] = (m < M) ? asgp[static_cast<size_t>(m) * G + g] : 0.f;
-      rs[i] = (m < M) ? rsp[static_cast<size_t>(m) * G + g] : 0.f;
-    }
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * kq + i;
+          as[i] = (m < M) ? s_as[m * G + g] : 0.f;
+          rs[i] = (m < M) ? s_rs[m * G + g] : 0.f;
+        }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float2 f = sz_factors(sz[static_cast<size_t>(g) * N + n0 + 16 * t + col]);
-      const v4f T = mfma_fp8(a, unpack_codes(bw[t]));
+        for (int t = 0; t < NT; ++t) {
+          const float2 f = sz_factors(zw[sl][t]);
+          const v4f T = mfma_fp8(av[sl], unpack_codes(bw[sl][t]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[t][i] += as[i] * (f.x * T[i] - f.y * rs[i]);
+          for (int i = 0; i < 4; ++i) acc[t][i] += as[i] * (f.x * T[i] - f.y * rs[i]);
+        }
+      }
     }
   }
 
-  __shared__ float sred[WV][16][16 * NT];
+  __syncthreads();   // the scale arrays are no longer read: the reduction reuses that LDS
+  float* sred = dsm;  // [WV][16][16 NT]
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sred[wave][4 * kq + i][16 * t + col] = acc[t][i];
+    for (int i = 0; i < 4; ++i) sred[(wave * 16 + 4 * kq + i) * 16 * NT + 16 * t + col] = acc[t][i];
   __syncthreads();
   const int outs = M * 16 * NT;
-  for (int idx = threadIdx.x; idx < outs; idx += 64 * WV) {
+  for (int idx = tid; idx < outs; idx += 64 * WV) {
     const int m = idx / (16 * NT), c = idx % (16 * NT);
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < WV; ++w) s += sred[w][m][c];
+    for (int w = 0; w < WV; ++w) s += sred[(w * 16 + m) * 16 * NT + c];
     y[static_cast<size_t>(m) * ldy + n0 + c] = static_cast<uint16_t>(f32_to_bf16(s));
   }
 }
 
-// ---------------------------------------------------------------------------------------
-// prefill: 128x128 output tile per 256-thread workgroup, 2x2 waves of 64x64, one 128-group
-// per k-step, operands staged in LDS in fragment order (double buffered).
-constexpr int kPBM = 128, kPBN = 128;
+template <int NT, int WV>
+size_t decode_dyn_lds(int M, int G) {
+  const size_t scales = static_cast<size_t>(2) * M * G * 4;
+  const size_t red = static_cast<size_t>(WV) * 16 * 16 * NT * 4;
+  return scales > red ? scales : red;
+}
 
-__global__ __launch_bounds__(256) void gemm_prefill_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ ASG, const float* __restrict__ RS,
-    int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ sz, int N,
-    int pb1, int pb2, uint16_t* __restrict__ y, int64_t ldy) {
+// ---------------------------------------------------------------------------------------
+// prefill: one 512-thread workgroup per CU-sized 256x256 output tile, 8 waves as 2 (rows) x 4
+// (columns) of 128x64, one 128-group per k-step. Operands move global -> LDS by direct LDS DMA
+// through a 3-stage ring (2 groups ahead); LDS images are in fragment order so every lane reads
+// 16 contiguous bytes. Per group and wave: 32 products T = MFMA(A_g, codes_g), each folded as
+// acc += (asg * 512 sc) * T (2 VALU per output), issued one row-fragment ahead of its fold so
+// the matrix core and the VALU overlap. After the loop the zero-point term is subtracted as a
+// bf16 matrix-core product (pack_zpe_kernel / zpe_act_kernel operands) and bf16 results are
+// stored for rows < M, columns < N. Tiles are numbered so that the ones an XCD runs at the
+// same time share their activation rows and weight columns in that XCD's L2.
+constexpr int kTM = 256, kTN = 256, kStages = 3;
+constexpr int kOffA = 0;          // [16 mf][2 half][64 lanes][16 B] = 32 KiB
+constexpr int kOffB = 32768;      // [16 nf][64 lanes][16 B]          = 16 KiB
+constexpr int kOffAsg = 49152;    // [256] f32
+constexpr int kOffSz = 50176;     // [256] u32
+constexpr int kStageBytes = 51200;
+
+// Direct global -> LDS DMA: lane l's 16 (or 4) bytes land at LDS address m0 + 16 l (4 l).
+// Issued as inline asm so the compiler does not see the LDS write: it would otherwise wait for
+// every outstanding request before each LDS read. Completion is tracked explicitly with
+// s_waitcnt vmcnt before the workgroup barrier (vmcnt completes in order, so the compiler's
+// own waits on its loads stay correct).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin; give each XCD a contiguous range of
+// tile numbers, and number tiles rows-fastest so that a range covers few column tiles.
+__device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
+  const int q = ntiles / 8;
+  return bid < 8 * q ? (bid % 8) * q + bid / 8 : bid;
+}
+
+__global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ ASG,
+    int M, int K, const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe,
+    const u32x4* __restrict__ zpa, const uint32_t* __restrict__ sz, int N, int pb1, int pb2,
+    uint16_t* __restrict__ y, int64_t ldy) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   const int G = K >> 7;
-  const int tiles_n = (N + kPBN - 1) / kPBN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  const int m0 = tm * kPBM, n0 = tn * kPBN;
+  const int tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
+  const int t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+  const int m0 = (t % tiles_m) * kTM, n0 = (t / tiles_m) * kTN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int col = lane & 15, kq = lane >> 4;
+  const int last_tile = N / 16 - 1;
+
+  // the tile's partition (the launcher guarantees boundaries are multiples of 256 here)
   const int p = (n0 >= pb1) + (n0 >= pb2);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // Per-lane DMA sources for group 0. A rows past M and column tiles past N are clamped to
+  // valid memory; their results are never stored.
+  const uint8_t* srcA[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = wave * 4 + i, mf = j >> 1, h = j & 1;
+    const int row = min(m0 + 16 * mf + (lane & 15), M - 1);
+    srcA[i] = A + (static_cast<size_t>(p) * M + row) * K + 32 * (lane >> 4) + 16 * h;
+  }
+  const uint8_t* srcB[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int nf = wave * 2 + i;
+    const int tt = min(n0 / 16 + nf, last_tile);
+    srcB[i] = reinterpret_cast<const uint8_t*>(wpk + static_cast<size_t>(tt) * G * 64 + lane);
+  }
+  const void* srcS;
+  if (wave < 4) srcS = ASG + (static_cast<size_t>(p) * M + min(m0 + 64 * wave + lane, M - 1)) * G;
+  else srcS = sz + min(n0 + 64 * (wave - 4) + lane, N - 1);
+
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int stage, int g) {
+    const uint32_t st = lds0 + stage * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(srcA[i] + 128 * g, st + kOffA + (wave * 4 + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16(srcB[i] + static_cast<size_t>(g) * 1024, st + kOffB + (wave * 2 + i) * 1024);
+    if (wave < 4) lds_dma4(static_cast<const float*>(srcS) + g, st + kOffAsg + wave * 256);
+    else lds_dma4(static_cast<const uint32_t*>(srcS) + static_cast<size_t>(g) * N, st + kOffSz + (wave - 4) * 256);
+  };
+
+  v4f acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  if (G > 1) issue(1, 1);
+  for (int g = 0; g < G; ++g) {
+    // This wave's DMA for group g has landed once at most the 7 requests of group g+1 are
+    // outstanding; the barrier then makes every wave's group-g data visible and guarantees no
+    // wave still reads stage (g+2)%3. (__syncthreads would also drain the group g+1 requests.)
+    if (g + 1 < G) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (g + 2 < G) issue((g + 2) % kStages, g + 2);
+    const uint8_t* st = smem + (g % kStages) * kStageBytes;
+
+    v8i bf[4];
+    float s9[4];
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+      bf[nf] = unpack_codes(*reinterpret_cast<const u32x4*>(st + kOffB + (wn * 4 + nf) * 1024 + lane * 16));
+      s9[nf] = f16_to_f32(*reinterpret_cast<const uint32_t*>(st + kOffSz + (wn * 64 + 16 * nf + col) * 4)) * 512.0f;
+    }
+    // products for row fragment mf are issued before the fold of mf-1
+    v4f Tb[2][4];
+    float4 asb[2];
+#pragma unroll
+    for (int mf = 0; mf <= 8; ++mf) {
+      if (mf < 8) {
+        const uint8_t* ap = st + kOffA + ((wm * 8 + mf) * 2) * 1024 + lane * 16;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 1024);
+        const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        asb[mf & 1] = *reinterpret_cast<const float4*>(st + kOffAsg + (wm * 128 + 16 * mf + 4 * kq) * 4);
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) Tb[mf & 1][nf] = mfma_fp8(a, bf[nf]);
+      }
+      if (mf > 0) {
+        const int pm = mf - 1;
+        const float4 as = asb[pm & 1];
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+          acc[pm][nf][0] = __builtin_fmaf(as.x * s9[nf], Tb[pm & 1][nf][0], acc[pm][nf][0]);
+          acc[pm][nf][1] = __builtin_fmaf(as.y * s9[nf], Tb[pm & 1][nf][1], acc[pm][nf][1]);
+          acc[pm][nf][2] = __builtin_fmaf(as.z * s9[nf], Tb[pm & 1][nf][2], acc[pm][nf][2]);
+          acc[pm][nf][3] = __builtin_fmaf(as.w * s9[nf], Tb[pm & 1][nf][3], acc[pm][nf][3]);
+        }
+      }
+    }
+  }
+
+  // ---- zero-point epilogue: acc += (-[a1|a1|a2]) x [z1;z2;z1] over KC chunks of 32 k'
+  {
+    const int KC = zpe_chunks(G), MT = (M + 15) / 16;
+    const u32x4* zab = zpa + static_cast<size_t>(p) * MT * KC * 64 + lane;
+    for (int c = 0; c < KC; ++c) {
+      u32x4 zb[4], za[8];
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) {
+        const int tt = min(n0 / 16 + wn * 4 + nf, last_tile);
+        zb[nf] = zpe[(static_cast<size_t>(tt) * KC + c) * 64 + lane];
+      }
+#pragma unroll
+      for (int mf = 0; mf < 8; ++mf) {
+        const int mt = min((m0 + wm * 128) / 16 + mf, MT - 1);
+        za[mf] = zab[(static_cast<size_t>(mt) * KC + c) * 64];
+      }
+#pragma unroll
+      for (int mf = 0; mf < 8; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[mf]),
+                                                                 __builtin_bit_cast(bf16x8, zb[nf]), acc[mf][nf], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int nf = 0; nf < 4; ++nf) {
+    const int n = n0 + wn * 64 + 16 * nf + col;
+    if (n >= N) continue;
+#pragma unroll
+    for (int mf = 0; mf < 8; ++mf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 128 + 16 * mf + 4 * kq + i;
+        if (m < M) y[static_cast<size_t>(m) * ldy + n] = static_cast<uint16_t>(f32_to_bf16(acc[mf][nf][i]));
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// prefill, 128-wide tiles (used when a partition boundary is not a multiple of 256):
+// 128x128 output tile per 256-thread workgroup, 2x2 waves of 64x64, one 128-group per
+// k-step. Operands move global -> LDS by direct LDS DMA (no register staging) through a
+// 3-stage ring; the LDS images are in fragment order so every lane reads 16 contiguous bytes.
+// Per group: T = MFMA(A_g, codes_g) for 16 fragments, then acc += (asg * 512 sc) * T
+// (2 VALU per output). After the loop the zero-point term is subtracted as one bf16
+// matrix-core product (see pack_zpe_kernel), then bf16 results are stored for rows < M.
+constexpr int kBM = 128, kBN = 128, kStages128 = 3;
+constexpr int kOffA128 = 0;                    // [8 mf][2 half][64 lanes][16 B]
+constexpr int kOffB128 = 16384;                // [8 nf][64 lanes][16 B]
+constexpr int kOffAsg128 = 24576;              // [128] f32
+constexpr int kOffSz128 = 25088;               // [128] u32
+constexpr int kStageBytes128 = 25600;
+
+__global__ __launch_bounds__(256, 2) void gemm_prefill128_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ ASG,
+    int M, int K, const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe,
+    const u32x4* __restrict__ zpa, const uint32_t* __restrict__ sz, int N, int pb1, int pb2,
+    uint16_t* __restrict__ y, int64_t ldy) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages128 * kStageBytes128];
+  const int G = K >> 7;
+  const int tiles_n = (N + kBN - 1) / kBN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int p = (n0 >= pb1) + (n0 >= pb2);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS DMA bases stay scalar
   const int wm = wave >> 1, wn = wave & 1;
   const int col = lane & 15, kq = lane >> 4;
 
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kPBM / 16][64 * 32];  // 2 x 16 KiB
-  __shared__ __attribute__((aligned(16))) u32x4 sB[2][kPBN / 16][64];         // 2 x 8 KiB
-  __shared__ __attribute__((aligned(16))) float sAsg[2][kPBM];
-  __shared__ __attribute__((aligned(16))) float sRs[2][kPBM];
-  __shared__ __attribute__((aligned(16))) uint32_t sSz[2][kPBN];
-
   const uint8_t* Ab = A + static_cast<size_t>(p) * M * K;
   const float* asgp = ASG + static_cast<size_t>(p) * M * G;
-  const float* rsp = RS + static_cast<size_t>(p) * M * G;
+    const int last_tile = N / 16 - 1;
 
-  // global -> register staging for one group
-  uint4 ra[4];
-  u32x4 rb[2];
-  float rscal;
-  uint32_t rsz;
-  auto load_group = [&](int g) {
+  // Per-lane DMA sources (group 0); rows past M and column tiles past N are clamped to valid
+  // memory — their results are never stored.
+  const uint8_t* srcA[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j;          // 16-byte chunk 0..1023 of the 128x128 A tile
-      const int r = c >> 3, part = c & 7;
-      const int m = m0 + r;
-      ra[j] = (m < M) ? *reinterpret_cast<const uint4*>(Ab + static_cast<size_t>(m) * K + 128 * g + 16 * part)
-                      : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int j = wave * 4 + i, mf = j >> 1, h = j & 1;
+    const int row = min(m0 + 16 * mf + (lane & 15), M - 1);
+    srcA[i] = Ab + static_cast<size_t>(row) * K + 32 * (lane >> 4) + 16 * h;
+  }
+  const uint8_t* srcB[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = tid + 256 * j;          // 16-byte chunk 0..511 of the 8 fragments
-      const int f = c >> 6, l = c & 63;
-      const int n = n0 + 16 * f;
-      rb[j] = (n < N) ? wpk[(static_cast<size_t>(n / 16) * G + g) * 64 + l] : u32x4{0u, 0u, 0u, 0u};
-    }
-    {
-      const int r = tid & 127, m = m0 + r;
-      const float* src = (tid < 128) ? asgp : rsp;
-      rscal = (m < M) ? src[static_cast<size_t>(m) * G + g] : 0.f;
-      const int n = n0 + (tid & 127);
-      rsz = (tid < 128 && n < N) ? sz[static_cast<size_t>(g) * N + n] : 0u;
-    }
-  };
-  auto store_group = [&](int buf) {
+  for (int i = 0; i < 2; ++i) {
+    const int nf = wave * 2 + i;
+    const int t = min(n0 / 16 + nf, last_tile);
+    srcB[i] = reinterpret_cast<const uint8_t*>(wpk + static_cast<size_t>(t) * G * 64 + lane);
+  }
+  const void* srcS;
+  if (wave < 2) srcS = asgp + static_cast<size_t>(min(m0 + 64 * wave + lane, M - 1)) * G;
+  else srcS = sz + min(n0 + 64 * (wave - 2) + lane, N - 1);
+
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int stage, int g) {
+    const uint32_t st = lds0 + stage * kStageBytes128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j;
-      const int r = c >> 3, part = c & 7;
-      const int mf = r >> 4, fl = (r & 15) + 16 * (part >> 1);
-      *reinterpret_cast<uint4*>(&sA[buf][mf][fl * 32 + 16 * (part & 1)]) = ra[j];
-    }
+    for (int i = 0; i < 4; ++i) lds_dma16(srcA[i] + 128 * g, st + kOffA128 + (wave * 4 + i) * 1024);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = tid + 256 * j;
-      sB[buf][c >> 6][c & 63] = rb[j];
-    }
-    if (tid < 128) { sAsg[buf][tid] = rscal; sSz[buf][tid] = rsz; }
-    else sRs[buf][tid - 128] = rscal;
+    for (int i = 0; i < 2; ++i) lds_dma16(srcB[i] + static_cast<size_t>(g) * 1024, st + kOffB128 + (wave * 2 + i) * 1024);
+    if (wave < 2) lds_dma4(static_cast<const float*>(srcS) + g, st + kOffAsg128 + wave * 256);
+    else lds_dma4(static_cast<const uint32_t*>(srcS) + static_cast<size_t>(g) * N, st + kOffSz128 + (wave - 2) * 256);
   };
 
   v4f acc[4][4];
@@ -245,52 +539,97 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  load_group(0);
-  store_group(0);
-  __syncthreads();
+  issue(0, 0);
+  if (G > 1) issue(1, 1);
   for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    if (g + 1 < G) load_group(g + 1);
-    // B fragments and their scale factors
+    // This wave's DMA for group g has landed once at most the 7 requests of group g+1 are
+    // outstanding; the barrier then makes every wave's group-g data visible and guarantees no
+    // wave still reads stage (g+2)%3. (__syncthreads would also drain the group g+1 requests.)
+    if (g + 1 < G) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (g + 2 < G) issue((g + 2) % kStages128, g + 2);
+    const uint8_t* st = smem + (g % kStages128) * kStageBytes128;
+
     v8i bf[4];
-    float2 fz[4];
+    float s9[4];
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) {
-      bf[nf] = unpack_codes(sB[buf][wn * 4 + nf][lane]);
-      fz[nf] = sz_factors(sSz[buf][wn * 64 + 16 * nf + col]);
+      bf[nf] = unpack_codes(*reinterpret_cast<const u32x4*>(st + kOffB128 + (wn * 4 + nf) * 1024 + lane * 16));
+      s9[nf] = f16_to_f32(*reinterpret_cast<const uint32_t*>(st + kOffSz128 + (wn * 64 + 16 * nf + col) * 4)) * 512.0f;
     }
+    // all 16 products of the group first (distinct result registers), then the folds: the
+    // matrix core works through the queue while the VALU folds finished results
+    v4f T[4][4];
+    float4 as[4];
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf) {
-      const uint4* ap = reinterpret_cast<const uint4*>(&sA[buf][wm * 4 + mf][lane * 32]);
-      const uint4 a0 = ap[0], a1 = ap[1];
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(st + kOffA128 + ((wm * 4 + mf) * 2 + 0) * 1024 + lane * 16);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(st + kOffA128 + ((wm * 4 + mf) * 2 + 1) * 1024 + lane * 16);
       const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      const float4 as = *reinterpret_cast<const float4*>(&sAsg[buf][wm * 64 + 16 * mf + 4 * kq]);
-      const float4 rs = *reinterpret_cast<const float4*>(&sRs[buf][wm * 64 + 16 * mf + 4 * kq]);
+      as[mf] = *reinterpret_cast<const float4*>(st + kOffAsg128 + (wm * 64 + 16 * mf + 4 * kq) * 4);
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) T[mf][nf] = mfma_fp8(a, bf[nf]);
+    }
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf) {
-        const v4f T = mfma_fp8(a, bf[nf]);
-        acc[mf][nf][0] += as.x * (fz[nf].x * T[0] - fz[nf].y * rs.x);
-        acc[mf][nf][1] += as.y * (fz[nf].x * T[1] - fz[nf].y * rs.y);
-        acc[mf][nf][2] += as.z * (fz[nf].x * T[2] - fz[nf].y * rs.z);
-        acc[mf][nf][3] += as.w * (fz[nf].x * T[3] - fz[nf].y * rs.w);
+        acc[mf][nf][0] = __builtin_fmaf(as[mf].x * s9[nf], T[mf][nf][0], acc[mf][nf][0]);
+        acc[mf][nf][1] = __builtin_fmaf(as[mf].y * s9[nf], T[mf][nf][1], acc[mf][nf][1]);
+        acc[mf][nf][2] = __builtin_fmaf(as[mf].z * s9[nf], T[mf][nf][2], acc[mf][nf][2]);
+        acc[mf][nf][3] = __builtin_fmaf(as[mf].w * s9[nf], T[mf][nf][3], acc[mf][nf][3]);
       }
+  }
+
+  // ---- zero-point epilogue: acc += (-[a1|a1|a2]) x [z1;z2;z1] over KC chunks of 32 k'
+  {
+    const int KC = zpe_chunks(G), MT = (M + 15) / 16;
+    const u32x4* zab = zpa + static_cast<size_t>(p) * MT * KC * 64 + lane;
+    for (int c = 0; c < KC; ++c) {
+      bf16x8 zb[4], za[4];
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) {
+        const int t = min(n0 / 16 + wn * 4 + nf, last_tile);
+        zb[nf] = __builtin_bit_cast(bf16x8, zpe[(static_cast<size_t>(t) * KC + c) * 64 + lane]);
+      }
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf) {
+        const int mt = min((m0 + wm * 64) / 16 + mf, MT - 1);
+        za[mf] = __builtin_bit_cast(bf16x8, zab[(static_cast<size_t>(mt) * KC + c) * 64]);
+      }
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za[mf], zb[nf], acc[mf][nf], 0, 0, 0);
     }
-    if (g + 1 < G) store_group(buf ^ 1);
-    __syncthreads();
   }
 
 #pragma unroll
-  for (int mf = 0; mf < 4; ++mf)
+  for (int nf = 0; nf < 4; ++nf) {
+    const int n = n0 + wn * 64 + 16 * nf + col;
+    if (n >= N) continue;
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
-      const int n = n0 + wn * 64 + 16 * nf + col;
-      if (n >= N) continue;
+    for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = m0 + wm * 64 + 16 * mf + 4 * kq + i;
         if (m < M) y[static_cast<size_t>(m) * ldy + n] = static_cast<uint16_t>(f32_to_bf16(acc[mf][nf][i]));
       }
-    }
+  }
+}
+
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 static int launch_status(const char* what) {
@@ -304,8 +643,10 @@ static int launch_status(const char* what) {
 extern "C" {
 
 size_t pq_packed_weight_bytes(int K, int N) {
-  if (K <= 0 || N <= 0) return 0;
-  return static_cast<size_t>(K) * static_cast<size_t>(N) / 2;
+  if (K <= 0 || N <= 0 || K % PQ_GROUP || N % 16) return 0;
+  const size_t codes = static_cast<size_t>(K) * static_cast<size_t>(N) / 2;
+  const size_t zpe = static_cast<size_t>(N / 16) * pq::zpe_chunks(K / PQ_GROUP) * 1024;
+  return codes + zpe;
 }
 
 int pq_pack_weights(const int32_t* qweight_d, const int32_t* qzeros_d, const uint16_t* scales_d,
@@ -318,18 +659,24 @@ int pq_pack_weights(const int32_t* qweight_d, const int32_t* qzeros_d, const uin
   if (!aligned(qweight_d, 4) || !aligned(qzeros_d, 4) || !aligned(scales_d, 2) || !aligned(wpk_d, 16) || !aligned(sz_d, 4))
     return set_error(PQ_ERR_ALIGN, "pq_pack_weights: misaligned pointer");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int G = K / PQ_GROUP;
   const int64_t words = static_cast<int64_t>(K) * N / 8;
   hipLaunchKernelGGL(pack_weights_kernel, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, s,
                      qweight_d, K, N, static_cast<uint32_t*>(wpk_d));
-  const int64_t gn = static_cast<int64_t>(K / PQ_GROUP) * N;
+  const int64_t gn = static_cast<int64_t>(G) * N;
   hipLaunchKernelGGL(pack_sz_kernel, dim3(static_cast<unsigned>((gn + 255) / 256)), dim3(256), 0, s,
-                     qzeros_d, scales_d, K / PQ_GROUP, N, reinterpret_cast<uint32_t*>(sz_d));
+                     qzeros_d, scales_d, G, N, reinterpret_cast<uint32_t*>(sz_d));
+  const int64_t zl = static_cast<int64_t>(N / 16) * zpe_chunks(G) * 64;
+  u32x4* zpe = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(wpk_d) + static_cast<size_t>(K) * N / 2);
+  hipLaunchKernelGGL(pack_zpe_kernel, dim3(static_cast<unsigned>((zl + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(sz_d), G, N, zpe);
   return launch_status("pq_pack_weights");
 }
 
 size_t pq_gemm_workspace_bytes(int M, int N, int K) {
-  (void)M; (void)N; (void)K;
-  return 0;
+  (void)N;
+  if (M <= 16 || K <= 0 || K % PQ_GROUP) return 0;     // the decode kernel needs none
+  return pq::zpe_act_bytes(M, K / PQ_GROUP, PQ_MAX_PARTITIONS);
 }
 
 int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
@@ -337,7 +684,6 @@ int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, in
             int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream) {
   using namespace pq;
   clear_error();
-  (void)ws_d;
   if (M < 0) return set_error(PQ_ERR_SHAPE, "pq_gemm: M=%d < 0", M);
   if (K <= 0 || K % PQ_GROUP || K > (1 << 24)) return set_error(PQ_ERR_SHAPE, "pq_gemm: K=%d must be a positive multiple of 128", K);
   if (N <= 0 || N % 16 || N > (1 << 24)) return set_error(PQ_ERR_SHAPE, "pq_gemm: N=%d must be a positive multiple of 16", N);
@@ -347,25 +693,55 @@ int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, in
   if (ws_bytes < pq_gemm_workspace_bytes(M, N, K)) return set_error(PQ_ERR_WORKSPACE, "pq_gemm: workspace too small");
   if (M == 0) return PQ_OK;
   if (!a_d || !asg_d || !rs_d || !wpk_d || !sz_d || !y_d) return set_error(PQ_ERR_NULL, "pq_gemm: NULL pointer");
-  if (!aligned(a_d, 16) || !aligned(asg_d, 4) || !aligned(rs_d, 4) || !aligned(wpk_d, 16) || !aligned(sz_d, 4) || !aligned(y_d, 4))
+  if (pq_gemm_workspace_bytes(M, N, K) && !ws_d) return set_error(PQ_ERR_NULL, "pq_gemm: NULL workspace");
+  if (!aligned(a_d, 16) || !aligned(asg_d, 4) || !aligned(rs_d, 4) || !aligned(wpk_d, 16) || !aligned(sz_d, 4) ||
+      !aligned(y_d, 4) || !aligned(ws_d, 16))
     return set_error(PQ_ERR_ALIGN, "pq_gemm: misaligned pointer");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int G = K / PQ_GROUP;
   const u32x4* wpk = static_cast<const u32x4*>(wpk_d);
   const uint32_t* sz = reinterpret_cast<const uint32_t*>(sz_d);
   if (M <= 16) {
-    if (N % 64 == 0) {
-      hipLaunchKernelGGL((gemm_decode_kernel<4, 8>), dim3(N / 64), dim3(512), 0, s,
+    // column block per workgroup: 64 columns if that still gives >= 256 workgroups
+    if (N % 64 == 0 && N / 64 >= 256) {
+      const size_t lds = decode_dyn_lds<4, 4>(M, G);
+      hipLaunchKernelGGL((gemm_decode_kernel<4, 4>), dim3(N / 64), dim3(256), lds, s,
+                         a_d, asg_d, rs_d, M, K, wpk, sz, N, pb1, pb2, y_d, ldy);
+    } else if (N % 32 == 0 && N / 32 >= 256) {
+      const size_t lds = decode_dyn_lds<2, 8>(M, G);
+      hipLaunchKernelGGL((gemm_decode_kernel<2, 8>), dim3(N / 32), dim3(512), lds, s,
                          a_d, asg_d, rs_d, M, K, wpk, sz, N, pb1, pb2, y_d, ldy);
     } else {
-      hipLaunchKernelGGL((gemm_decode_kernel<1, 8>), dim3(N / 16), dim3(512), 0, s,
+      const size_t lds = decode_dyn_lds<1, 8>(M, G);
+      hipLaunchKernelGGL((gemm_decode_kernel<1, 8>), dim3(N / 16), dim3(512), lds, s,
                          a_d, asg_d, rs_d, M, K, wpk, sz, N, pb1, pb2, y_d, ldy);
     }
     return launch_status("pq_gemm(decode)");
   }
-  const int64_t tiles = static_cast<int64_t>((M + kPBM - 1) / kPBM) * ((N + kPBN - 1) / kPBN);
+  // 256x256 tiles (one workgroup per CU) move half the bytes per output of 128x128 tiles (two
+  // per CU); take them unless a partition boundary is not on a 256-column line or they fill the
+  // CUs' last round of tiles worse.
+  const int64_t t256 = static_cast<int64_t>((M + kTM - 1) / kTM) * ((N + kTN - 1) / kTN);
+  const int64_t t128 = static_cast<int64_t>((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int cus = cu_count();
+  auto fill = [](int64_t tiles, int64_t slots) {
+    return static_cast<double>(tiles) / (static_cast<double>((tiles + slots - 1) / slots) * slots);
+  };
+  const bool aligned256 = (pb1 >= N || pb1 % kTN == 0) && (pb2 >= N || pb2 % kTN == 0);
+  const bool wide = aligned256 && fill(t256, cus) >= fill(t128, 2 * cus) - 1e-9;
+  const int64_t tiles = wide ? t256 : t128;
   if (tiles > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "pq_gemm: problem too large");
-  hipLaunchKernelGGL(gemm_prefill_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s,
-                     a_d, asg_d, rs_d, M, K, wpk, sz, N, pb1, pb2, y_d, ldy);
+  const u32x4* zpe = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(wpk_d) + static_cast<size_t>(K) * N / 2);
+  u32x4* zpa = static_cast<u32x4*>(ws_d);
+  const int64_t zt = static_cast<int64_t>(P) * ((M + 15) / 16) * zpe_chunks(G) * 64;
+  hipLaunchKernelGGL(zpe_act_kernel, dim3(static_cast<unsigned>((zt + 255) / 256)), dim3(256), 0, s,
+                     asg_d, rs_d, M, G, P, zpa);
+  if (wide)
+    hipLaunchKernelGGL(gemm_prefill_kernel, dim3(static_cast<unsigned>(tiles)), dim3(512), 0, s,
+                       a_d, asg_d, M, K, wpk, zpe, zpa, sz, N, pb1, pb2, y_d, ldy);
+  else
+    hipLaunchKernelGGL(gemm_prefill128_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s,
+                       a_d, asg_d, M, K, wpk, zpe, zpa, sz, N, pb1, pb2, y_d, ldy);
   return launch_status("pq_gemm(prefill)");
 }
 

@@ -123,6 +123,8 @@ def test_gemm_m0_is_noop_and_partition_ok():
     assert _gemm(M=0, P=3, N=8192, pb1=6144, pb2=7168, ldy=8192) == 0
     assert _gemm(M=0, P=2, N=256, pb1=128, ldy=256) == 0
     assert pq.gemm_workspace_bytes(8, 17408, 5120) == 0
+    assert pq.gemm_workspace_bytes(2048, 17408, 5120) == 3 * 128 * 4 * 1024
+    assert _gemm(M=32, ws=None, ws_bytes=1 << 20) == -1
 
 
 def _rq(**kw):
@@ -151,7 +153,10 @@ def test_pack_validation():
     assert L.pq_pack_weights(FAKE, FAKE, FAKE, 256, 8, FAKE, FAKE, None) == -2
     assert L.pq_pack_weights(None, FAKE, FAKE, 256, 128, FAKE, FAKE, None) == -1
     assert L.pq_pack_weights(FAKE, FAKE, FAKE, 256, 128, ctypes.c_void_p(0x100008), FAKE, None) == -3
-    assert L.pq_packed_weight_bytes(5120, 17408) == 5120 * 17408 // 2
+    # codes (K*N/2) + the zero-point epilogue operand: N/16 tiles x ceil(3G/32) chunks x 1 KiB
+    assert L.pq_packed_weight_bytes(5120, 17408) == 5120 * 17408 // 2 + (17408 // 16) * 4 * 1024
+    assert L.pq_packed_weight_bytes(17408, 5120) == 17408 * 5120 // 2 + (5120 // 16) * 13 * 1024
+    assert L.pq_packed_weight_bytes(100, 16) == 0
 
 
 def test_hooks_validation():
