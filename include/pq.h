@@ -80,7 +80,8 @@ int pq_build_records(const int16_t* pairs_h, const uint16_t* theta_h, int K, voi
  *           column 8j + (0,2,4,6,1,3,5,7)[i]; zero points stored as-is (section "Format").
  * scales_d  f16 [K/128, N].
  * wpk_d     out, pq_packed_weight_bytes(K, N) bytes: first K*N/2 bytes hold the same 4-bit
- *           codes reordered into matrix-core fragment order (1 KiB per 16 columns x 128-group);
+ *           codes reordered into matrix-core fragment order (1 KiB per 16 columns x 128-group,
+ *           each 16-column strip's groups contiguous);
  *           then, per 16 columns, ceil(3*(K/128)/32) KiB of bf16 operands for the zero-point
  *           epilogue (the f32 values 8*sc + fl16(sc*(zp-8)) split into two bf16 pieces).
  *           Returns 0 for shapes the library rejects.

@@ -14,11 +14,13 @@
 //     sc * sum_k D(a_k)(c_k - 8) - zsc * rs = (512 sc) * T - (8 sc + zsc) * rs,
 // both factors exact in fp32 (512 sc is a power-of-two scaling, 8 sc + zsc needs < 24 bits).
 //
-// Packed weight layout (pq_pack_weights): for each 16-column tile t and group g, 1 KiB at
-// ((t * G + g) * 1024): lane l (column 16t + l%16, k = 128g + 32*(l/16) + 0..31) owns 16 bytes
+// Packed weight layout (pq_pack_weights), tile-major so that one column tile's whole K extent
+// is one contiguous run: for 16-column tile t and group g, 1 KiB at ((t * G + g) * 1024): lane l (column 16t + l%16, k = 128g + 32*(l/16) + 0..31) owns 16 bytes
 // = 4 words; byte b of word q holds code(k0 + 8q + b) in its low nibble and code(k0 + 8q + 4 + b)
 // in its high nibble. (w & 0x0F0F0F0F) and ((w >> 4) & 0x0F0F0F0F) are then the lane's B
 // operand registers 2q and 2q+1, matching the A operand's 32 consecutive k bytes.
+#include <algorithm>
+
 #include "pq_device.h"
 #include "pq_internal.h"
 
@@ -67,12 +69,12 @@ __global__ void pack_weights_kernel(const int32_t* __restrict__ qweight, int K, 
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = static_cast<int64_t>(K) * N / 8;
   if (idx >= total) return;
-  const int G = K >> 7;
   const int q = static_cast<int>(idx & 3);
   const int l = static_cast<int>((idx >> 2) & 63);
   const int64_t rest = idx >> 8;
-  const int g = static_cast<int>(rest % G);
+  const int G = K >> 7;
   const int t = static_cast<int>(rest / G);
+  const int g = static_cast<int>(rest % G);
   const int n = 16 * t + (l & 15);
   const int k0 = 128 * g + 32 * (l >> 4) + 8 * q;
   const int shift = awq_shift(n);
@@ -173,118 +175,226 @@ size_t zpe_act_bytes(int M, int G, int P) {
 }
 
 // ---------------------------------------------------------------------------------------
-// decode: M <= 16. One workgroup per 16*NT columns; its WV waves split the groups (partial sums
-// meet in LDS). Each wave runs a 3-slot register ring over its groups: the loads of group g+2
-// (weights, activation fragment, SZ words) are issued before group g is computed, so two
-// groups are always in flight and no load waits on another. The per-(row, group) scales are
-// staged in LDS once per workgroup with all their loads issued together.
-template <int NT, int WV>
-__global__ __launch_bounds__(64 * WV, (WV == 4 ? 3 : 4)) void gemm_decode_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ ASG, const float* __restrict__ RS,
-    int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ sz, int N,
-    int pb1, int pb2, uint16_t* __restrict__ y, int64_t ldy) {
-  extern __shared__ __attribute__((aligned(16))) float dsm[];   // [M*G] asg, [M*G] rs; later the reduction
+// Direct global -> LDS loads (64 lanes x 4 or 16 bytes to M0 + lane * size; inactive lanes write
+// nothing)
+// Issued as inline asm so the compiler does not see the LDS write: it would otherwise wait for
+// every outstanding request before each LDS read. Completion is tracked explicitly with
+// s_waitcnt vmcnt before the workgroup barrier (vmcnt completes in order, so the compiler's
+// own waits on its loads stay correct).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ void lds_dma16_on(const void* g, uint32_t lds, bool on) {
+  if (on) lds_dma16(g, lds);
+}
+__device__ __forceinline__ void lds_dma4_on(const void* g, uint32_t lds, bool on) {
+  if (on) lds_dma4(g, lds);
+}
+// scalar base + per-lane 32-bit offset: the per-group address arithmetic stays on the SALU
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_dma4_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------------------------------
+// decode: M <= 16, a stream of the packed weights. A CU's memory pipeline delivers a bounded
+// rate, so the kernel time is set by the CU with the most bytes: the column tiles (16 columns
+// each) are dealt out so that every CU streams the same amount. The grid is a multiple of the
+// CU count; each workgroup takes a contiguous run of 1..kDecMaxNT tiles inside one partition,
+// runs differing by at most one tile (DecodeMap). The 4 waves of a workgroup split the groups;
+// their partial sums meet in LDS at the end.
+// Each wave streams its groups through a private LDS ring of D slots with direct LDS loads: a
+// slot holds one group's NT weight tiles, the activation fragment, the SZ words and the rows'
+// asg/rs values. Group g+D-1 is requested before group g is computed and an explicit vmcnt wait
+// covers exactly group g, so D-1 groups stay in flight. The loads are invisible to the
+// compiler, which therefore never inserts waits of its own on them (register rings lose their
+// depth to such waits when the allocator copies an in-flight register). Two workgroups share a
+// CU so that two waves per SIMD hide each other's LDS and matrix-core latencies.
+constexpr int kDecWaves = 4;
+constexpr int kDecMaxNT = 6;
+constexpr int kDecRingBytes = 20480;   // per wave
+constexpr int kDecLds = kDecWaves * kDecRingBytes;
+constexpr int kDecPerCU = 2;           // workgroups resident per CU (LDS-bound)
+struct DecodeMap {
+  int wg0[4];   // first workgroup of partition q; wg0[3] = grid size
+  int t0[3];    // first tile of partition q
+  int nt[3];    // tiles of partition q
+};
+
+template <int NT>
+struct DecodeSlot {
+  static constexpr int kSzLoads = (NT + 3) / 4;                 // 64 SZ words per load
+  static constexpr int kOffA = NT * 1024;                       // [2 halves][64 lanes][16 B]
+  static constexpr int kOffSz = (NT + 2) * 1024;                // [16 NT] words
+  static constexpr int kOffSc = kOffSz + kSzLoads * 256;        // [16] asg, [16] rs
+  static constexpr int kBytes = kOffSc + 128;
+  static constexpr int kDepth = kDecRingBytes / kBytes > 16 ? 16 : kDecRingBytes / kBytes;
+  static constexpr int kLoads = NT + 2 + kSzLoads + 2;          // loads per group
+  static_assert(kDepth >= 2 && (kDepth - 1) * kLoads <= 63, "decode ring does not fit vmcnt");
+};
+
+// MR = activation rows held per lane that can be live (1 when M == 1, else 4)
+template <int NT, int MR>
+__device__ __forceinline__ void decode_body(
+    const uint8_t* __restrict__ A, const float* __restrict__ asgp, const float* __restrict__ rsp,
+    int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ sz, int N, int p,
+    int tfirst, uint16_t* __restrict__ y, int64_t ldy, uint8_t* smem) {
+  using S = DecodeSlot<NT>;
+  constexpr int D = S::kDepth;
   const int G = K >> 7;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
   const int col = lane & 15, kq = lane >> 4;
-  const int n0 = blockIdx.x * (16 * NT);
-  const int p = (n0 >= pb1) + (n0 >= pb2);
-  const int g0 = (G * wave) / WV, g1 = (G * (wave + 1)) / WV;
+  const int n0 = 16 * tfirst;
+  const int g0 = (G * wave) / kDecWaves, g1 = (G * (wave + 1)) / kDecWaves;
 
-  const bool arow = col < M;  // A operand row = lane % 16
-  const uint8_t* Ap = A + (static_cast<size_t>(p) * M + (arow ? col : 0)) * K + 32 * kq;
-  const u32x4* wp = wpk + static_cast<size_t>(n0 / 16) * G * 64 + lane;
-  const uint32_t* szp = sz + n0 + col;
+  // Sources: a scalar base per group plus a fixed per-lane offset. A operand row = lane % 16:
+  // lanes with row >= M load nothing and their products land in output rows that are never
+  // stored; the same holds for scale rows >= M.
+  const uint8_t* wbase = reinterpret_cast<const uint8_t*>(wpk) + static_cast<size_t>(tfirst) * G * 1024;
+  const uint32_t woff = 16 * lane;
+  const bool a_on = col < M;
+  const uint8_t* abase = A + static_cast<size_t>(p) * M * K;
+  const uint32_t aoff = static_cast<uint32_t>((a_on ? col : 0) * K + 32 * kq);
+  const uint8_t* zbase = reinterpret_cast<const uint8_t*>(sz + n0);
+  const uint32_t zoff = 4 * lane;
+  const int srow = lane & 15;
+  const bool as_on = lane < 16 && srow < M, rs_on = lane >= 16 && lane < 32 && srow < M;
+  const uint32_t soff = static_cast<uint32_t>(4 * (srow < M ? srow : 0) * G);
 
-  u32x4 bw[3][NT];
-  uint32_t zw[3][NT];
-  v8i av[3];
-  auto issue = [&](int slot, int g) {
-    if (g < g1) {
+  uint8_t* ringp = smem + wave * kDecRingBytes;
+  const uint32_t ring = lds_addr(ringp);
+  auto issue = [&](int g, int slot) {
+    const uint32_t sb = ring + slot * S::kBytes;
+    const uint8_t* wg = wbase + static_cast<size_t>(g) * 1024;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bw[slot][t] = __builtin_nontemporal_load(wp + (static_cast<size_t>(t) * G + g) * 64);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) zw[slot][t] = szp[static_cast<size_t>(g) * N + 16 * t];
-      av[slot] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      if (arow) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(Ap + 128 * g);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(Ap + 128 * g + 16);
-        av[slot] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      }
+    for (int t = 0; t < NT; ++t) lds_dma16_s(wg + static_cast<size_t>(t) * G * 1024, woff, sb + t * 1024);
+    if (a_on) {
+      lds_dma16_s(abase + 128 * g, aoff, sb + S::kOffA);
+      lds_dma16_s(abase + 128 * g + 16, aoff, sb + S::kOffA + 1024);
     }
+    const uint8_t* zg = zbase + static_cast<size_t>(g) * N * 4;
+#pragma unroll
+    for (int j = 0; j < S::kSzLoads; ++j)
+      if (lane + 64 * j < 16 * NT) lds_dma4_s(zg + 256 * j, zoff, sb + S::kOffSz + j * 256);
+    if (as_on) lds_dma4_s(asgp + g, soff, sb + S::kOffSc);
+    if (rs_on) lds_dma4_s(rsp + g, soff, sb + S::kOffSc);
   };
-  issue(0, g0);
-  issue(1, g0 + 1);
-
-  float* s_as = dsm;
-  float* s_rs = dsm + M * G;
-  const float* asgp = ASG + static_cast<size_t>(p) * M * G;
-  const float* rsp = RS + static_cast<size_t>(p) * M * G;
-  for (int i0 = 0; i0 < M * G; i0 += 4 * 64 * WV) {
-    float va[4], vr[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 64 * WV + tid;
-      va[u] = (i < M * G) ? asgp[i] : 0.f;
-      vr[u] = (i < M * G) ? rsp[i] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 64 * WV + tid;
-      if (i < M * G) { s_as[i] = va[u]; s_rs[i] = vr[u]; }
-    }
-  }
-  __syncthreads();
+  // Each load above has a live lane in every wave (lane 0 for weights, A, SZ and asg; lane 16
+  // for rs), so each one is issued and counted by vmcnt.
+  const int ng = g1 - g0;
+  for (int i = 0; i < D - 1 && i < ng; ++i) issue(g0 + i, i);
 
   v4f acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int gb = g0; gb < g1; gb += 3) {
-#pragma unroll
-    for (int sl = 0; sl < 3; ++sl) {
-      const int g = gb + sl;
-      if (g < g1) {
-        issue((sl + 2) % 3, g + 2);
-        float as[4], rs[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 4 * kq + i;
-          as[i] = (m < M) ? s_as[m * G + g] : 0.f;
-          rs[i] = (m < M) ? s_rs[m * G + g] : 0.f;
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const float2 f = sz_factors(zw[sl][t]);
-          const v4f T = mfma_fp8(av[sl], unpack_codes(bw[sl][t]));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[t][i] += as[i] * (f.x * T[i] - f.y * rs[i]);
-        }
-      }
+  int slot = 0;
+  for (int g = g0; g < g1; ++g) {
+    if (g + D - 1 < g1) {
+      issue(g + D - 1, slot == 0 ? D - 1 : slot - 1);
+      wait_vm<(D - 1) * S::kLoads>();   // group g has landed; D-1 groups remain in flight
+    } else {
+      wait_vm<0>();
     }
+    const uint8_t* sp = ringp + slot * S::kBytes;
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(sp + S::kOffA + 16 * lane);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(sp + S::kOffA + 1024 + 16 * lane);
+    const v8i av = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    const v4f as = *reinterpret_cast<const v4f*>(sp + S::kOffSc + 16 * kq);
+    const v4f rs = *reinterpret_cast<const v4f*>(sp + S::kOffSc + 64 + 16 * kq);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 bw = *reinterpret_cast<const u32x4*>(sp + t * 1024 + 16 * lane);
+      const float2 f = sz_factors(*reinterpret_cast<const uint32_t*>(sp + S::kOffSz + 4 * (16 * t + col)));
+      const v4f T = mfma_fp8(av, unpack_codes(bw));
+#pragma unroll
+      for (int i = 0; i < MR; ++i) acc[t][i] += as[i] * (f.x * T[i] - f.y * rs[i]);
+    }
+    slot = slot + 1 == D ? 0 : slot + 1;
   }
 
-  __syncthreads();   // the scale arrays are no longer read: the reduction reuses that LDS
-  float* sred = dsm;  // [WV][16][16 NT]
+  __syncthreads();   // every ring has drained: the reduction reuses that LDS
+  float* sred = reinterpret_cast<float*>(smem);   // [waves][16][16 NT]
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) sred[(wave * 16 + 4 * kq + i) * 16 * NT + 16 * t + col] = acc[t][i];
   __syncthreads();
   const int outs = M * 16 * NT;
-  for (int idx = tid; idx < outs; idx += 64 * WV) {
+  for (int idx = tid; idx < outs; idx += 64 * kDecWaves) {
     const int m = idx / (16 * NT), c = idx % (16 * NT);
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < WV; ++w) s += sred[(w * 16 + m) * 16 * NT + c];
+    for (int w = 0; w < kDecWaves; ++w) s += sred[(w * 16 + m) * 16 * NT + c];
     y[static_cast<size_t>(m) * ldy + n0 + c] = static_cast<uint16_t>(f32_to_bf16(s));
   }
 }
 
-template <int NT, int WV>
-size_t decode_dyn_lds(int M, int G) {
-  const size_t scales = static_cast<size_t>(2) * M * G * 4;
-  const size_t red = static_cast<size_t>(WV) * 16 * 16 * NT * 4;
-  return scales > red ? scales : red;
+__global__ __launch_bounds__(64 * kDecWaves, kDecPerCU) void gemm_decode_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ ASG, const float* __restrict__ RS,
+    int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ sz, int N,
+    DecodeMap map, uint16_t* __restrict__ y, int64_t ldy) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kDecLds];
+  const int b = blockIdx.x;
+  const int q = (b >= map.wg0[1]) + (b >= map.wg0[2]);          // partition
+  const int nwq = map.wg0[q + 1] - map.wg0[q], bq = b - map.wg0[q];
+  const int base = map.nt[q] / nwq, extra = map.nt[q] % nwq;
+  const int cnt = base + (bq < extra);
+  const int tfirst = map.t0[q] + bq * base + (bq < extra ? bq : extra);
+  const size_t MG = static_cast<size_t>(M) * (K >> 7);
+  const float* asgp = ASG + q * MG;
+  const float* rsp = RS + q * MG;
+#define PQ_DECODE_CASE(n)                                                                      \
+  case n:                                                                                      \
+    if (M == 1) decode_body<n, 1>(A, asgp, rsp, M, K, wpk, sz, N, q, tfirst, y, ldy, smem);   \
+    else decode_body<n, 4>(A, asgp, rsp, M, K, wpk, sz, N, q, tfirst, y, ldy, smem);          \
+    break;
+  switch (cnt) {
+    PQ_DECODE_CASE(1) PQ_DECODE_CASE(2) PQ_DECODE_CASE(3)
+    PQ_DECODE_CASE(4) PQ_DECODE_CASE(5) PQ_DECODE_CASE(6)
+    default: break;
+  }
+#undef PQ_DECODE_CASE
+}
+
+// Deals the N/16 column tiles out to workgroups: a grid that is a multiple of the resident
+// workgroup slots (kDecPerCU per CU), each workgroup taking at most kDecMaxNT tiles per round,
+// split over the partitions in proportion to their tiles; returns the largest run of tiles any
+// workgroup gets.
+int decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
+  const int NTT = N / 16;
+  const int tb[4] = {0, pb1 < N ? pb1 / 16 : NTT, pb2 < N ? pb2 / 16 : NTT, NTT};
+  const int64_t slots = static_cast<int64_t>(kDecPerCU) * cus;
+  const int64_t rounds = (NTT + kDecMaxNT * slots - 1) / (kDecMaxNT * slots);
+  const int64_t W = std::min<int64_t>(NTT, rounds * slots);
+  int maxrun = 0, wg = 0;
+  for (int q = 0; q < 3; ++q) {
+    const int nt = tb[q + 1] - tb[q];
+    map->wg0[q] = wg;
+    map->t0[q] = tb[q];
+    map->nt[q] = nt;
+    if (nt <= 0) continue;
+    int64_t w = (W * nt + NTT / 2) / NTT;
+    w = std::max<int64_t>(w, (nt + kDecMaxNT - 1) / kDecMaxNT);
+    w = std::min<int64_t>(std::max<int64_t>(w, 1), nt);
+    wg += static_cast<int>(w);
+    maxrun = std::max(maxrun, static_cast<int>((nt + w - 1) / w));
+  }
+  map->wg0[3] = wg;
+  return maxrun;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -305,20 +415,6 @@ constexpr int kOffSz = 50176;     // [256] u32
 constexpr int kStageBytes = 51200;
 
 // Direct global -> LDS DMA: lane l's 16 (or 4) bytes land at LDS address m0 + 16 l (4 l).
-// Issued as inline asm so the compiler does not see the LDS write: it would otherwise wait for
-// every outstanding request before each LDS read. Completion is tracked explicitly with
-// s_waitcnt vmcnt before the workgroup barrier (vmcnt completes in order, so the compiler's
-// own waits on its loads stay correct).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
-}
-
 // Workgroups are dispatched to the 8 XCDs round-robin; give each XCD a contiguous range of
 // tile numbers, and number tiles rows-fastest so that a range covers few column tiles.
 __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
@@ -702,20 +798,10 @@ int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, in
   const u32x4* wpk = static_cast<const u32x4*>(wpk_d);
   const uint32_t* sz = reinterpret_cast<const uint32_t*>(sz_d);
   if (M <= 16) {
-    // column block per workgroup: 64 columns if that still gives >= 256 workgroups
-    if (N % 64 == 0 && N / 64 >= 256) {
-      const size_t lds = decode_dyn_lds<4, 4>(M, G);
-      hipLaunchKernelGGL((gemm_decode_kernel<4, 4>), dim3(N / 64), dim3(256), lds, s,
-                         a_d, asg_d, rs_d, M, K, wpk, sz, N, pb1, pb2, y_d, ldy);
-    } else if (N % 32 == 0 && N / 32 >= 256) {
-      const size_t lds = decode_dyn_lds<2, 8>(M, G);
-      hipLaunchKernelGGL((gemm_decode_kernel<2, 8>), dim3(N / 32), dim3(512), lds, s,
-                         a_d, asg_d, rs_d, M, K, wpk, sz, N, pb1, pb2, y_d, ldy);
-    } else {
-      const size_t lds = decode_dyn_lds<1, 8>(M, G);
-      hipLaunchKernelGGL((gemm_decode_kernel<1, 8>), dim3(N / 16), dim3(512), lds, s,
-                         a_d, asg_d, rs_d, M, K, wpk, sz, N, pb1, pb2, y_d, ldy);
-    }
+    DecodeMap map;
+    decode_map(N, pb1, pb2, cu_count(), &map);
+    hipLaunchKernelGGL(gemm_decode_kernel, dim3(map.wg0[3]), dim3(64 * kDecWaves), 0, s,
+                       a_d, asg_d, rs_d, M, K, wpk, sz, N, map, y_d, ldy);
     return launch_status("pq_gemm(decode)");
   }
   // 256x256 tiles (one workgroup per CU) move half the bytes per output of 128x128 tiles (two
