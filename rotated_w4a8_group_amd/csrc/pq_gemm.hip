@@ -398,23 +398,73 @@ int decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
 }
 
 // ---------------------------------------------------------------------------------------
-// prefill: one 512-thread workgroup per CU-sized 256x256 output tile, 8 waves as 2 (rows) x 4
-// (columns) of 128x64, one 128-group per k-step. Operands move global -> LDS by direct LDS DMA
-// through a 3-stage ring (2 groups ahead); LDS images are in fragment order so every lane reads
-// 16 contiguous bytes. Per group and wave: 32 products T = MFMA(A_g, codes_g), each folded as
-// acc += (asg * 512 sc) * T (2 VALU per output), issued one row-fragment ahead of its fold so
-// the matrix core and the VALU overlap. After the loop the zero-point term is subtracted as a
-// bf16 matrix-core product (pack_zpe_kernel / zpe_act_kernel operands) and bf16 results are
-// stored for rows < M, columns < N. Tiles are numbered so that the ones an XCD runs at the
-// same time share their activation rows and weight columns in that XCD's L2.
-constexpr int kTM = 256, kTN = 256, kStages = 3;
-constexpr int kOffA = 0;          // [16 mf][2 half][64 lanes][16 B] = 32 KiB
-constexpr int kOffB = 32768;      // [16 nf][64 lanes][16 B]          = 16 KiB
-constexpr int kOffAsg = 49152;    // [256] f32
-constexpr int kOffSz = 50176;     // [256] u32
-constexpr int kStageBytes = 51200;
+// prefill (M > 16). One 512-thread workgroup (8 waves) per output tile of TM x TN; the waves
+// form a WM x WN grid of (TM/WM) x (TN/WN) blocks; one 128-group per k-step. Operands move
+// global -> LDS by direct LDS loads through a 3-stage ring (2 groups ahead); the LDS images are
+// in matrix-core fragment order so every lane reads 16 contiguous bytes. Per group and wave the
+// products T = MFMA(A_g, codes_g) are folded as acc += (asg * 512 sc) * T (2 VALU per output),
+// each row fragment's products issued before the previous fragment's fold. After the loop the
+// zero-point term is subtracted as a bf16 matrix-core product (pack_zpe_kernel / zpe_act_kernel
+// operands), and the bf16 tile is staged in LDS and written as whole rows.
+//
+// Tiles (PrefillMap): whole rounds of 256x256 tiles, one workgroup per CU; the tiles of the
+// last, partial round are cut into 2, 4 or 8 pieces (128x256, 128x128, 64x128) so that round
+// costs a fraction of a full one instead of a full round at low occupancy. Partition boundaries
+// that are not multiples of 256 switch the whole launch to 128x128 tiles (pieces 64x128).
+constexpr int kPfStages = 3;
+constexpr int kPfWaves = 8;
+constexpr int kPfLds = kPfStages * 51200;   // the 256x256 ring (the largest)
 
-// Direct global -> LDS DMA: lane l's 16 (or 4) bytes land at LDS address m0 + 16 l (4 l).
+template <int TM, int TN, int WM, int WN>
+struct PfTile {
+  static constexpr int MF = TM / WM / 16, NF = TN / WN / 16;   // fragments per wave
+  static constexpr int kOffA = 0;                              // [TM/16][2 halves][64 lanes][16 B]
+  static constexpr int kOffB = TM * 128;                       // [TN/16 tiles][64 lanes][16 B]
+  static constexpr int kOffAsg = kOffB + TN * 64;              // [TM] f32
+  static constexpr int kOffSz = kOffAsg + TM * 4;              // [TN] u32
+  static constexpr int kStage = (kOffSz + TN * 4 + 255) / 256 * 256;
+  static constexpr int nA = TM / 8, nB = TN / 16, nAs = TM / 64, nSz = TN / 64;
+  static constexpr int nD = nA + nB + nAs + nSz;                // direct loads per group
+  static constexpr int kPerWave = (nD + kPfWaves - 1) / kPfWaves;
+  static constexpr int kOutStride = TN + 8;                    // bf16 per staged output row
+  static_assert(WM * WN == kPfWaves && MF >= 1 && NF >= 1 && TM % 64 == 0 && TN % 64 == 0, "tile");
+  static_assert(kPfStages * kStage <= kPfLds && TM * kOutStride * 2 <= kPfLds, "LDS");
+  static_assert(kPerWave <= 31, "vmcnt");
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Writes an LDS-staged bf16 tile [TM rows][STRIDE] to y (rows < M, columns < N): 16-byte stores
+// of 8 columns when y and ldy allow it (vec16), else 4-byte stores of 2 columns. Uses all threads
+// of the workgroup.
+template <int TM, int TN, int STRIDE>
+__device__ __forceinline__ void store_tile_rows(const uint16_t* ot, uint16_t* __restrict__ y, int64_t ldy,
+                                                int m0, int n0, int M, int N, bool vec16) {
+  const int nthr = blockDim.x;
+  if (vec16) {
+    constexpr int CH = TN / 8;
+    for (int c = threadIdx.x; c < TM * CH; c += nthr) {
+      const int r = c / CH, ch = c % CH;
+      const int m = m0 + r, n = n0 + 8 * ch;
+      if (m < M && n < N)
+        *reinterpret_cast<u32x4*>(y + static_cast<size_t>(m) * ldy + n) =
+            *reinterpret_cast<const u32x4*>(ot + r * STRIDE + 8 * ch);
+    }
+  } else {
+    constexpr int CH = TN / 2;
+    for (int c = threadIdx.x; c < TM * CH; c += nthr) {
+      const int r = c / CH, ch = c % CH;
+      const int m = m0 + r, n = n0 + 2 * ch;
+      if (m < M && n < N)
+        *reinterpret_cast<uint32_t*>(y + static_cast<size_t>(m) * ldy + n) =
+            *reinterpret_cast<const uint32_t*>(ot + r * STRIDE + 2 * ch);
+    }
+  }
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin; give each XCD a contiguous range of
 // tile numbers, and number tiles rows-fastest so that a range covers few column tiles.
 __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
@@ -422,99 +472,113 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
   return bid < 8 * q ? (bid % 8) * q + bid / 8 : bid;
 }
 
-__global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ ASG,
-    int M, int K, const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe,
-    const u32x4* __restrict__ zpa, const uint32_t* __restrict__ sz, int N, int pb1, int pb2,
-    uint16_t* __restrict__ y, int64_t ldy) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+template <int TM, int TN, int WM, int WN>
+__device__ __forceinline__ void prefill_tile(
+    const uint8_t* __restrict__ A, const float* __restrict__ ASG, int M, int K,
+    const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe, const u32x4* __restrict__ zpa,
+    const uint32_t* __restrict__ sz, int N, int p, int m0, int n0, uint16_t* __restrict__ y,
+    int64_t ldy, bool vec16, uint8_t* smem) {
+  using TL = PfTile<TM, TN, WM, WN>;
+  constexpr int MF = TL::MF, NF = TL::NF, PW = TL::kPerWave;
   const int G = K >> 7;
-  const int tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
-  const int t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
-  const int m0 = (t % tiles_m) * kTM, n0 = (t / tiles_m) * kTN;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: load table stays scalar
+  const int wm = wave / WN, wn = wave % WN;
   const int col = lane & 15, kq = lane >> 4;
   const int last_tile = N / 16 - 1;
+  const float* asgp = ASG + static_cast<size_t>(p) * M * G;
 
-  // the tile's partition (the launcher guarantees boundaries are multiples of 256 here)
-  const int p = (n0 >= pb1) + (n0 >= pb2);
-
-  // Per-lane DMA sources for group 0. A rows past M and column tiles past N are clamped to
-  // valid memory; their results are never stored.
-  const uint8_t* srcA[4];
+  // This wave's share of the group's direct loads: entry d = wave + 8 i of the tile's list (A
+  // half-fragments, weight tiles, asg rows, SZ columns), taken modulo the list length so every
+  // wave issues PW loads (a repeated entry writes the same bytes again). Each entry is a scalar
+  // base (advanced per group on the scalar unit) plus a fixed 32-bit lane offset. Rows past M
+  // and column tiles past N are clamped to valid memory; their results are never stored.
+  const uint8_t* sbase[PW];
+  uint32_t voff[PW];
+  size_t step[PW];
+  uint32_t dst[PW];
+  bool wide[PW];
+  const uint8_t* Ap = A + static_cast<size_t>(p) * M * K;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = wave * 4 + i, mf = j >> 1, h = j & 1;
-    const int row = min(m0 + 16 * mf + (lane & 15), M - 1);
-    srcA[i] = A + (static_cast<size_t>(p) * M + row) * K + 32 * (lane >> 4) + 16 * h;
+  for (int i = 0; i < PW; ++i) {
+    const int d = (wave + kPfWaves * i) % TL::nD;
+    if (d < TL::nA) {
+      const int mf = d >> 1, h = d & 1;
+      const int row = min(m0 + 16 * mf + (lane & 15), M - 1);
+      sbase[i] = Ap;
+      voff[i] = static_cast<uint32_t>(row * K + 32 * (lane >> 4) + 16 * h);
+      step[i] = 128; dst[i] = TL::kOffA + d * 1024; wide[i] = true;
+    } else if (d < TL::nA + TL::nB) {
+      const int j = d - TL::nA;
+      const int tt = min(n0 / 16 + j, last_tile);
+      sbase[i] = reinterpret_cast<const uint8_t*>(wpk) + static_cast<size_t>(tt) * G * 1024;
+      voff[i] = 16 * lane;
+      step[i] = 1024; dst[i] = TL::kOffB + j * 1024; wide[i] = true;
+    } else if (d < TL::nA + TL::nB + TL::nAs) {
+      const int j = d - TL::nA - TL::nB;
+      sbase[i] = reinterpret_cast<const uint8_t*>(asgp);
+      voff[i] = static_cast<uint32_t>(min(m0 + 64 * j + lane, M - 1) * G * 4);
+      step[i] = 4; dst[i] = TL::kOffAsg + j * 256; wide[i] = false;
+    } else {
+      const int j = d - TL::nA - TL::nB - TL::nAs;
+      sbase[i] = reinterpret_cast<const uint8_t*>(sz);
+      voff[i] = static_cast<uint32_t>(min(n0 + 64 * j + lane, N - 1) * 4);
+      step[i] = static_cast<size_t>(N) * 4; dst[i] = TL::kOffSz + j * 256; wide[i] = false;
+    }
   }
-  const uint8_t* srcB[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int nf = wave * 2 + i;
-    const int tt = min(n0 / 16 + nf, last_tile);
-    srcB[i] = reinterpret_cast<const uint8_t*>(wpk + static_cast<size_t>(tt) * G * 64 + lane);
-  }
-  const void* srcS;
-  if (wave < 4) srcS = ASG + (static_cast<size_t>(p) * M + min(m0 + 64 * wave + lane, M - 1)) * G;
-  else srcS = sz + min(n0 + 64 * (wave - 4) + lane, N - 1);
-
   const uint32_t lds0 = lds_addr(smem);
   auto issue = [&](int stage, int g) {
-    const uint32_t st = lds0 + stage * kStageBytes;
+    const uint32_t st = lds0 + stage * TL::kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(srcA[i] + 128 * g, st + kOffA + (wave * 4 + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) lds_dma16(srcB[i] + static_cast<size_t>(g) * 1024, st + kOffB + (wave * 2 + i) * 1024);
-    if (wave < 4) lds_dma4(static_cast<const float*>(srcS) + g, st + kOffAsg + wave * 256);
-    else lds_dma4(static_cast<const uint32_t*>(srcS) + static_cast<size_t>(g) * N, st + kOffSz + (wave - 4) * 256);
+    for (int i = 0; i < PW; ++i) {
+      if (wide[i]) lds_dma16_s(sbase[i] + g * step[i], voff[i], st + dst[i]);
+      else lds_dma4_s(sbase[i] + g * step[i], voff[i], st + dst[i]);
+    }
   };
 
-  v4f acc[8][4];
+  v4f acc[MF][NF];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NF; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   issue(0, 0);
   if (G > 1) issue(1, 1);
   for (int g = 0; g < G; ++g) {
-    // This wave's DMA for group g has landed once at most the 7 requests of group g+1 are
+    // This wave's loads for group g have landed once at most the PW loads of group g+1 are
     // outstanding; the barrier then makes every wave's group-g data visible and guarantees no
-    // wave still reads stage (g+2)%3. (__syncthreads would also drain the group g+1 requests.)
-    if (g + 1 < G) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (g + 2 < G) issue((g + 2) % kStages, g + 2);
-    const uint8_t* st = smem + (g % kStages) * kStageBytes;
+    // wave still reads stage (g+2)%3. (__syncthreads would also drain the group g+1 loads.)
+    if (g + 1 < G) wait_vm_lgkm_barrier<PW>();
+    else wait_vm_lgkm_barrier<0>();
+    if (g + 2 < G) issue((g + 2) % kPfStages, g + 2);
+    const uint8_t* st = smem + (g % kPfStages) * TL::kStage;
 
-    v8i bf[4];
-    float s9[4];
+    v8i bf[NF];
+    float s9[NF];
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
-      bf[nf] = unpack_codes(*reinterpret_cast<const u32x4*>(st + kOffB + (wn * 4 + nf) * 1024 + lane * 16));
-      s9[nf] = f16_to_f32(*reinterpret_cast<const uint32_t*>(st + kOffSz + (wn * 64 + 16 * nf + col) * 4)) * 512.0f;
+    for (int nf = 0; nf < NF; ++nf) {
+      bf[nf] = unpack_codes(*reinterpret_cast<const u32x4*>(st + TL::kOffB + (wn * NF + nf) * 1024 + lane * 16));
+      s9[nf] = f16_to_f32(*reinterpret_cast<const uint32_t*>(st + TL::kOffSz + (wn * NF * 16 + 16 * nf + col) * 4)) * 512.0f;
     }
-    // products for row fragment mf are issued before the fold of mf-1
-    v4f Tb[2][4];
+    // the products of row fragment mf are issued before the fold of mf-1
+    v4f Tb[2][NF];
     float4 asb[2];
 #pragma unroll
-    for (int mf = 0; mf <= 8; ++mf) {
-      if (mf < 8) {
-        const uint8_t* ap = st + kOffA + ((wm * 8 + mf) * 2) * 1024 + lane * 16;
+    for (int mf = 0; mf <= MF; ++mf) {
+      if (mf < MF) {
+        const uint8_t* ap = st + TL::kOffA + ((wm * MF + mf) * 2) * 1024 + lane * 16;
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 1024);
         const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        asb[mf & 1] = *reinterpret_cast<const float4*>(st + kOffAsg + (wm * 128 + 16 * mf + 4 * kq) * 4);
+        asb[mf & 1] = *reinterpret_cast<const float4*>(st + TL::kOffAsg + (wm * MF * 16 + 16 * mf + 4 * kq) * 4);
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) Tb[mf & 1][nf] = mfma_fp8(a, bf[nf]);
+        for (int nf = 0; nf < NF; ++nf) Tb[mf & 1][nf] = mfma_fp8(a, bf[nf]);
       }
       if (mf > 0) {
         const int pm = mf - 1;
         const float4 as = asb[pm & 1];
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
+        for (int nf = 0; nf < NF; ++nf) {
           acc[pm][nf][0] = __builtin_fmaf(as.x * s9[nf], Tb[pm & 1][nf][0], acc[pm][nf][0]);
           acc[pm][nf][1] = __builtin_fmaf(as.y * s9[nf], Tb[pm & 1][nf][1], acc[pm][nf][1]);
           acc[pm][nf][2] = __builtin_fmaf(as.z * s9[nf], Tb[pm & 1][nf][2], acc[pm][nf][2]);
@@ -524,195 +588,115 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
     }
   }
 
-  // ---- zero-point epilogue: acc += (-[a1|a1|a2]) x [z1;z2;z1] over KC chunks of 32 k'
+  // ---- zero-point epilogue: acc += (-[a1|a1|a2]) x [z1;z2;z1] over KC chunks of 32 k'. The
+  // operands of CB chunks are requested together (a chunk index past KC re-reads the last
+  // chunk and is not used).
   {
+    constexpr int CB = MF >= 8 ? 2 : 4;
     const int KC = zpe_chunks(G), MT = (M + 15) / 16;
     const u32x4* zab = zpa + static_cast<size_t>(p) * MT * KC * 64 + lane;
-    for (int c = 0; c < KC; ++c) {
-      u32x4 zb[4], za[8];
+    for (int c0 = 0; c0 < KC; c0 += CB) {
+      u32x4 zb[CB][NF], za[CB][MF];
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const int tt = min(n0 / 16 + wn * 4 + nf, last_tile);
-        zb[nf] = zpe[(static_cast<size_t>(tt) * KC + c) * 64 + lane];
+      for (int j = 0; j < CB; ++j) {
+        const int c = min(c0 + j, KC - 1);
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) {
+          const int tt = min(n0 / 16 + wn * NF + nf, last_tile);
+          zb[j][nf] = zpe[(static_cast<size_t>(tt) * KC + c) * 64 + lane];
+        }
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) {
+          const int mt = min(m0 / 16 + wm * MF + mf, MT - 1);
+          za[j][mf] = zab[(static_cast<size_t>(mt) * KC + c) * 64];
+        }
       }
 #pragma unroll
-      for (int mf = 0; mf < 8; ++mf) {
-        const int mt = min((m0 + wm * 128) / 16 + mf, MT - 1);
-        za[mf] = zab[(static_cast<size_t>(mt) * KC + c) * 64];
+      for (int j = 0; j < CB; ++j) {
+        if (c0 + j >= KC) break;
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf)
+            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[j][mf]),
+                                                                   __builtin_bit_cast(bf16x8, zb[j][nf]), acc[mf][nf], 0, 0, 0);
       }
-#pragma unroll
-      for (int mf = 0; mf < 8; ++mf)
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf)
-          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[mf]),
-                                                                 __builtin_bit_cast(bf16x8, zb[nf]), acc[mf][nf], 0, 0, 0);
     }
   }
 
+  // ---- bf16 tile through LDS (the ring is idle now), then whole rows with wide stores
+  __syncthreads();   // every wave has finished reading the ring
+  uint16_t* ot = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-  for (int nf = 0; nf < 4; ++nf) {
-    const int n = n0 + wn * 64 + 16 * nf + col;
-    if (n >= N) continue;
+  for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
-    for (int mf = 0; mf < 8; ++mf)
+    for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 128 + 16 * mf + 4 * kq + i;
-        if (m < M) y[static_cast<size_t>(m) * ldy + n] = static_cast<uint16_t>(f32_to_bf16(acc[mf][nf][i]));
-      }
+      for (int i = 0; i < 4; ++i)
+        ot[(wm * MF * 16 + 16 * mf + 4 * kq + i) * TL::kOutStride + wn * NF * 16 + 16 * nf + col] =
+            static_cast<uint16_t>(f32_to_bf16(acc[mf][nf][i]));
+  __syncthreads();
+  store_tile_rows<TM, TN, TL::kOutStride>(ot, y, ldy, m0, n0, M, N, vec16);
+}
+
+struct PrefillMap {
+  int tiles_m;   // whole tiles per tile column
+  int ntiles;    // whole tiles
+  int full;      // workgroups that run whole tiles (whole rounds); the rest run pieces
+  int split;     // pieces per remaining tile: 1, 2, 4 or 8 (wide) / 1 or 2 (narrow)
+  int wide;      // 1: 256x256 tiles, 0: 128x128 tiles
+};
+
+__global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ ASG, int M, int K,
+    const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe, const u32x4* __restrict__ zpa,
+    const uint32_t* __restrict__ sz, int N, int pb1, int pb2, uint16_t* __restrict__ y, int64_t ldy,
+    PrefillMap map, bool vec16) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfLds];
+  const int b = blockIdx.x;
+  const int bt = map.wide ? 256 : 128;
+  const bool piece = b >= map.full;
+  const int big = piece ? map.full + (b - map.full) / map.split : b;
+  const int r = piece ? (b - map.full) % map.split : 0;
+  const int t = xcd_tile(big, map.ntiles);
+  int m0 = (t % map.tiles_m) * bt, n0 = (t / map.tiles_m) * bt;
+  const int split = piece ? map.split : 1;
+  // piece r of a whole tile: split 2 -> 2 row halves; 4 -> 2 x 2 quarters; 8 -> 4 row x 2 column
+  if (split == 2) m0 += (bt / 2) * r;
+  else if (split == 4) { m0 += 128 * (r & 1); n0 += 128 * (r >> 1); }
+  else if (split == 8) { m0 += 64 * (r & 3); n0 += 128 * (r >> 2); }
+  if (m0 >= M || n0 >= N) return;   // a piece wholly past the matrix
+  const int p = (n0 >= pb1) + (n0 >= pb2);
+  if (map.wide) {
+    if (split == 1) prefill_tile<256, 256, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 2) prefill_tile<128, 256, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 4) prefill_tile<128, 128, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+  } else {
+    if (split == 1) prefill_tile<128, 128, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
   }
 }
 
-// ---------------------------------------------------------------------------------------
-// prefill, 128-wide tiles (used when a partition boundary is not a multiple of 256):
-// 128x128 output tile per 256-thread workgroup, 2x2 waves of 64x64, one 128-group per
-// k-step. Operands move global -> LDS by direct LDS DMA (no register staging) through a
-// 3-stage ring; the LDS images are in fragment order so every lane reads 16 contiguous bytes.
-// Per group: T = MFMA(A_g, codes_g) for 16 fragments, then acc += (asg * 512 sc) * T
-// (2 VALU per output). After the loop the zero-point term is subtracted as one bf16
-// matrix-core product (see pack_zpe_kernel), then bf16 results are stored for rows < M.
-constexpr int kBM = 128, kBN = 128, kStages128 = 3;
-constexpr int kOffA128 = 0;                    // [8 mf][2 half][64 lanes][16 B]
-constexpr int kOffB128 = 16384;                // [8 nf][64 lanes][16 B]
-constexpr int kOffAsg128 = 24576;              // [128] f32
-constexpr int kOffSz128 = 25088;               // [128] u32
-constexpr int kStageBytes128 = 25600;
-
-__global__ __launch_bounds__(256, 2) void gemm_prefill128_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ ASG,
-    int M, int K, const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe,
-    const u32x4* __restrict__ zpa, const uint32_t* __restrict__ sz, int N, int pb1, int pb2,
-    uint16_t* __restrict__ y, int64_t ldy) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages128 * kStageBytes128];
-  const int G = K >> 7;
-  const int tiles_n = (N + kBN - 1) / kBN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  const int m0 = tm * kBM, n0 = tn * kBN;
-  const int p = (n0 >= pb1) + (n0 >= pb2);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS DMA bases stay scalar
-  const int wm = wave >> 1, wn = wave & 1;
-  const int col = lane & 15, kq = lane >> 4;
-
-  const uint8_t* Ab = A + static_cast<size_t>(p) * M * K;
-  const float* asgp = ASG + static_cast<size_t>(p) * M * G;
-    const int last_tile = N / 16 - 1;
-
-  // Per-lane DMA sources (group 0); rows past M and column tiles past N are clamped to valid
-  // memory — their results are never stored.
-  const uint8_t* srcA[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = wave * 4 + i, mf = j >> 1, h = j & 1;
-    const int row = min(m0 + 16 * mf + (lane & 15), M - 1);
-    srcA[i] = Ab + static_cast<size_t>(row) * K + 32 * (lane >> 4) + 16 * h;
+// Whole rounds of tiles (one workgroup per CU), then the remaining tiles in pieces.
+PrefillMap prefill_map(int M, int N, bool wide, int cus) {
+  PrefillMap m{};
+  const int bt = wide ? 256 : 128;
+  m.wide = wide ? 1 : 0;
+  m.tiles_m = (M + bt - 1) / bt;
+  const int64_t nt = static_cast<int64_t>(m.tiles_m) * ((N + bt - 1) / bt);
+  m.ntiles = static_cast<int>(nt);
+  const int64_t full = (nt / cus) * cus, rem = nt - full;
+  m.full = static_cast<int>(full);
+  m.split = 1;
+  if (rem > 0) {
+    const int cands_wide[3] = {8, 4, 2}, cands_narrow[1] = {2};
+    const int* c = wide ? cands_wide : cands_narrow;
+    const int nc = wide ? 3 : 1;
+    for (int i = 0; i < nc; ++i)
+      if (rem * c[i] <= cus) { m.split = c[i]; break; }
   }
-  const uint8_t* srcB[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int nf = wave * 2 + i;
-    const int t = min(n0 / 16 + nf, last_tile);
-    srcB[i] = reinterpret_cast<const uint8_t*>(wpk + static_cast<size_t>(t) * G * 64 + lane);
-  }
-  const void* srcS;
-  if (wave < 2) srcS = asgp + static_cast<size_t>(min(m0 + 64 * wave + lane, M - 1)) * G;
-  else srcS = sz + min(n0 + 64 * (wave - 2) + lane, N - 1);
-
-  const uint32_t lds0 = lds_addr(smem);
-  auto issue = [&](int stage, int g) {
-    const uint32_t st = lds0 + stage * kStageBytes128;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(srcA[i] + 128 * g, st + kOffA128 + (wave * 4 + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) lds_dma16(srcB[i] + static_cast<size_t>(g) * 1024, st + kOffB128 + (wave * 2 + i) * 1024);
-    if (wave < 2) lds_dma4(static_cast<const float*>(srcS) + g, st + kOffAsg128 + wave * 256);
-    else lds_dma4(static_cast<const uint32_t*>(srcS) + static_cast<size_t>(g) * N, st + kOffSz128 + (wave - 2) * 256);
-  };
-
-  v4f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  issue(0, 0);
-  if (G > 1) issue(1, 1);
-  for (int g = 0; g < G; ++g) {
-    // This wave's DMA for group g has landed once at most the 7 requests of group g+1 are
-    // outstanding; the barrier then makes every wave's group-g data visible and guarantees no
-    // wave still reads stage (g+2)%3. (__syncthreads would also drain the group g+1 requests.)
-    if (g + 1 < G) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (g + 2 < G) issue((g + 2) % kStages128, g + 2);
-    const uint8_t* st = smem + (g % kStages128) * kStageBytes128;
-
-    v8i bf[4];
-    float s9[4];
-#pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
-      bf[nf] = unpack_codes(*reinterpret_cast<const u32x4*>(st + kOffB128 + (wn * 4 + nf) * 1024 + lane * 16));
-      s9[nf] = f16_to_f32(*reinterpret_cast<const uint32_t*>(st + kOffSz128 + (wn * 64 + 16 * nf + col) * 4)) * 512.0f;
-    }
-    // all 16 products of the group first (distinct result registers), then the folds: the
-    // matrix core works through the queue while the VALU folds finished results
-    v4f T[4][4];
-    float4 as[4];
-#pragma unroll
-    for (int mf = 0; mf < 4; ++mf) {
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(st + kOffA128 + ((wm * 4 + mf) * 2 + 0) * 1024 + lane * 16);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(st + kOffA128 + ((wm * 4 + mf) * 2 + 1) * 1024 + lane * 16);
-      const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      as[mf] = *reinterpret_cast<const float4*>(st + kOffAsg128 + (wm * 64 + 16 * mf + 4 * kq) * 4);
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf) T[mf][nf] = mfma_fp8(a, bf[nf]);
-    }
-#pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        acc[mf][nf][0] = __builtin_fmaf(as[mf].x * s9[nf], T[mf][nf][0], acc[mf][nf][0]);
-        acc[mf][nf][1] = __builtin_fmaf(as[mf].y * s9[nf], T[mf][nf][1], acc[mf][nf][1]);
-        acc[mf][nf][2] = __builtin_fmaf(as[mf].z * s9[nf], T[mf][nf][2], acc[mf][nf][2]);
-        acc[mf][nf][3] = __builtin_fmaf(as[mf].w * s9[nf], T[mf][nf][3], acc[mf][nf][3]);
-      }
-  }
-
-  // ---- zero-point epilogue: acc += (-[a1|a1|a2]) x [z1;z2;z1] over KC chunks of 32 k'
-  {
-    const int KC = zpe_chunks(G), MT = (M + 15) / 16;
-    const u32x4* zab = zpa + static_cast<size_t>(p) * MT * KC * 64 + lane;
-    for (int c = 0; c < KC; ++c) {
-      bf16x8 zb[4], za[4];
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const int t = min(n0 / 16 + wn * 4 + nf, last_tile);
-        zb[nf] = __builtin_bit_cast(bf16x8, zpe[(static_cast<size_t>(t) * KC + c) * 64 + lane]);
-      }
-#pragma unroll
-      for (int mf = 0; mf < 4; ++mf) {
-        const int mt = min((m0 + wm * 64) / 16 + mf, MT - 1);
-        za[mf] = __builtin_bit_cast(bf16x8, zab[(static_cast<size_t>(mt) * KC + c) * 64]);
-      }
-#pragma unroll
-      for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf)
-          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za[mf], zb[nf], acc[mf][nf], 0, 0, 0);
-    }
-  }
-
-#pragma unroll
-  for (int nf = 0; nf < 4; ++nf) {
-    const int n = n0 + wn * 64 + 16 * nf + col;
-    if (n >= N) continue;
-#pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 64 + 16 * mf + 4 * kq + i;
-        if (m < M) y[static_cast<size_t>(m) * ldy + n] = static_cast<uint16_t>(f32_to_bf16(acc[mf][nf][i]));
-      }
-  }
+  return m;
 }
 
 // Compute units of the current device (cached per device).
@@ -804,30 +788,25 @@ int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, in
                        a_d, asg_d, rs_d, M, K, wpk, sz, N, map, y_d, ldy);
     return launch_status("pq_gemm(decode)");
   }
-  // 256x256 tiles (one workgroup per CU) move half the bytes per output of 128x128 tiles (two
-  // per CU); take them unless a partition boundary is not on a 256-column line or they fill the
-  // CUs' last round of tiles worse.
-  const int64_t t256 = static_cast<int64_t>((M + kTM - 1) / kTM) * ((N + kTN - 1) / kTN);
-  const int64_t t128 = static_cast<int64_t>((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-  const int cus = cu_count();
-  auto fill = [](int64_t tiles, int64_t slots) {
-    return static_cast<double>(tiles) / (static_cast<double>((tiles + slots - 1) / slots) * slots);
-  };
-  const bool aligned256 = (pb1 >= N || pb1 % kTN == 0) && (pb2 >= N || pb2 % kTN == 0);
-  const bool wide = aligned256 && fill(t256, cus) >= fill(t128, 2 * cus) - 1e-9;
-  const int64_t tiles = wide ? t256 : t128;
-  if (tiles > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "pq_gemm: problem too large");
+  // 256x256 tiles (one workgroup per CU) unless a partition boundary is not on a 256-column line
+  const bool wide = (pb1 >= N || pb1 % 256 == 0) && (pb2 >= N || pb2 % 256 == 0);
+  const int bt = wide ? 256 : 128;
+  const int64_t tiles = static_cast<int64_t>((M + bt - 1) / bt) * ((N + bt - 1) / bt);
+  if (tiles * 8 > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "pq_gemm: problem too large");
+  // the prefill kernel addresses a partition's activations with 32-bit lane offsets
+  if (static_cast<int64_t>(M) * K > 0x7FFFFFFF || static_cast<int64_t>(M) * (K / PQ_GROUP) * 4 > 0x7FFFFFFF)
+    return set_error(PQ_ERR_SHAPE, "pq_gemm: M * K too large for one call (split the rows)");
+  const PrefillMap map = prefill_map(M, N, wide, cu_count());
+  const int64_t grid = static_cast<int64_t>(map.full) + static_cast<int64_t>(map.ntiles - map.full) * map.split;
   const u32x4* zpe = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(wpk_d) + static_cast<size_t>(K) * N / 2);
   u32x4* zpa = static_cast<u32x4*>(ws_d);
   const int64_t zt = static_cast<int64_t>(P) * ((M + 15) / 16) * zpe_chunks(G) * 64;
   hipLaunchKernelGGL(zpe_act_kernel, dim3(static_cast<unsigned>((zt + 255) / 256)), dim3(256), 0, s,
                      asg_d, rs_d, M, G, P, zpa);
-  if (wide)
-    hipLaunchKernelGGL(gemm_prefill_kernel, dim3(static_cast<unsigned>(tiles)), dim3(512), 0, s,
-                       a_d, asg_d, M, K, wpk, zpe, zpa, sz, N, pb1, pb2, y_d, ldy);
-  else
-    hipLaunchKernelGGL(gemm_prefill128_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s,
-                       a_d, asg_d, M, K, wpk, zpe, zpa, sz, N, pb1, pb2, y_d, ldy);
+  // 16-byte output stores need a 16-byte aligned y and a row pitch of 8 elements
+  const bool vec16 = aligned(y_d, 16) && ldy % 8 == 0;
+  hipLaunchKernelGGL(gemm_prefill_kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * kPfWaves), 0, s,
+                     a_d, asg_d, M, K, wpk, zpe, zpa, sz, N, pb1, pb2, y_d, ldy, map, vec16);
   return launch_status("pq_gemm(prefill)");
 }
 
