@@ -88,63 +88,114 @@ static double f16_to_double(uint16_t h) {
 
 // Lane order for the 64 pairs of one (layer, group).
 //
-// The prologue keeps a token's 128 channels in LDS in channel order (word c at bank c mod 64
-// and c mod 32) and updates a layer in place: lane l reads channel t_l, then channel h_l,
-// rotates, and writes both back. This picks for each pair which channel is read first
-// (t = "tail") and which lane it goes to so that
-//   * across the 64 lanes the tails are distinct mod 64 and so are the heads, and
-//   * within each half-wave (lanes 0-31, 32-63) tails and heads are distinct mod 32,
-// which makes every read and write conflict-free whether the LDS serves a wave in one pass
-// over 64 banks or in two half-wave passes over 32 banks.
+// The prologue keeps 4 tokens of a token-group in LDS token-minor: channel c occupies the
+// 16-byte row lds_row(c) = c + c/8 (one padding row per 8 channels). In each layer lane l reads
+// the row of its pair's first channel ("tail"), then the row of the second ("head"), rotates
+// the 4 tokens and writes both rows back. A 16-byte access by 64 lanes is served in passes of
+// 16 lanes over 64 banks or 8 lanes over 32 banks, so it is conflict-free when, in every block of
+// 16 lanes, the tails' rows are distinct mod 16 and the heads' rows too, and in every half-block
+// of 8 lanes they are distinct mod 8. This picks each pair's orientation (listing a pair as
+// (j, i) is the same rotation with sin negated) and its lane so that both hold.
 //
-// Tails mod 64: channels c and c^64 share a 64-bank; pair edges plus these sibling links form
-// even alternating cycles, so walking each cycle and taking every second channel as a tail
-// gives one tail per 64-bank. Halves: each 32-residue is then the tail of exactly two pairs
-// and the head of exactly two; linking pairs that share a tail residue or a head residue
-// gives even cycles again, and colouring each cycle alternately splits the pairs into two
-// halves of 32 with distinct residues.
-static void order_layer(const int* pi, const int* pj, int* tail, int* head, int* lane_of) {
-  int partner[128];
-  for (int q = 0; q < 64; ++q) { partner[pi[q]] = pj[q]; partner[pj[q]] = pi[q]; }
-  int pair_of[128];
-  for (int q = 0; q < 64; ++q) { pair_of[pi[q]] = q; pair_of[pj[q]] = q; }
-  bool done[64] = {false};
-  for (int q0 = 0; q0 < 64; ++q0) {
-    if (done[q0]) continue;
-    int t = pi[q0];
-    while (true) {
-      const int q = pair_of[t];
-      if (done[q]) break;
-      done[q] = true;
-      tail[q] = t;
-      head[q] = partner[t];
-      t = head[q] ^ 64;  // the sibling of a head must be a tail
+// Residues u = lds_row(c) mod 16 take each value for exactly 8 channels, so the pairs are the
+// edges of an 8-regular multigraph on 16 residues. Orienting every edge along an Euler circuit
+// gives each residue 4 outgoing and 4 incoming edges; the bipartite graph (outgoing side x
+// incoming side) is then 4-regular and splits into 4 perfect matchings, each one a block whose
+// 16 tails and 16 heads are all distinct residues. Inside a block, edges whose tails differ by 8
+// are linked, and so are edges whose heads differ by 8; the links form even alternating cycles,
+// and colouring each cycle alternately gives two half-blocks distinct mod 8.
+static int lds_row(int c) { return c + (c >> 3); }
+
+// Returns false only if a step that cannot fail for a valid pairing did (never expected).
+static bool order_layer(const int* pi, const int* pj, int* tail, int* head, int* lane_of) {
+  // residue multigraph and an Euler orientation (Hierholzer, iterative)
+  int ru[64], rv[64];
+  for (int q = 0; q < 64; ++q) { ru[q] = lds_row(pi[q]) & 15; rv[q] = lds_row(pj[q]) & 15; }
+  std::vector<int> adj[16];
+  for (int q = 0; q < 64; ++q) { adj[ru[q]].push_back(q); if (rv[q] != ru[q]) adj[rv[q]].push_back(q); else adj[ru[q]].push_back(q); }
+  bool used[64] = {false};
+  size_t ptr[16] = {0};
+  int from[64];   // residue the oriented edge leaves
+  for (int s = 0; s < 16; ++s) {
+    // walk circuits from s until all its edges are used; orientation = direction of travel
+    std::vector<int> stack{s};
+    while (!stack.empty()) {
+      const int v = stack.back();
+      while (ptr[v] < adj[v].size() && used[adj[v][ptr[v]]]) ++ptr[v];
+      if (ptr[v] == adj[v].size()) { stack.pop_back(); continue; }
+      const int q = adj[v][ptr[v]];
+      used[q] = true;
+      from[q] = v;
+      stack.push_back(ru[q] == v ? rv[q] : ru[q]);
     }
   }
-  // tail-mate / head-mate links by residue mod 32
-  int tmate[64], hmate[64];
-  int first_t[32], first_h[32];
-  for (int r = 0; r < 32; ++r) first_t[r] = first_h[r] = -1;
+  int tr[64], hr[64];   // tail / head residue of each oriented edge
   for (int q = 0; q < 64; ++q) {
-    const int rt = tail[q] & 31, rh = head[q] & 31;
-    if (first_t[rt] < 0) first_t[rt] = q; else { tmate[q] = first_t[rt]; tmate[first_t[rt]] = q; }
-    if (first_h[rh] < 0) first_h[rh] = q; else { hmate[q] = first_h[rh]; hmate[first_h[rh]] = q; }
+    const bool fwd = from[q] == ru[q];
+    tail[q] = fwd ? pi[q] : pj[q];
+    head[q] = fwd ? pj[q] : pi[q];
+    tr[q] = lds_row(tail[q]) & 15;
+    hr[q] = lds_row(head[q]) & 15;
   }
-  int color[64];
-  for (int q = 0; q < 64; ++q) color[q] = -1;
-  for (int q0 = 0; q0 < 64; ++q0) {
-    if (color[q0] >= 0) continue;
-    int q = q0, c = 0;
-    bool via_tail = true;
-    while (color[q] < 0) {
-      color[q] = c;
-      q = via_tail ? tmate[q] : hmate[q];
-      via_tail = !via_tail;
-      c ^= 1;
+  // split into 4 perfect matchings of the 4-regular bipartite multigraph tail residue -> head residue
+  int block[64];
+  bool taken[64] = {false};
+  for (int b = 0; b < 4; ++b) {
+    int match_h[16], match_t[16];   // head residue -> edge, tail residue -> edge
+    for (int r = 0; r < 16; ++r) match_h[r] = match_t[r] = -1;
+    for (int u = 0; u < 16; ++u) {
+      // augmenting path from tail residue u (Kuhn's algorithm over the untaken edges)
+      int prev_edge[16];
+      bool seen[16] = {false};
+      std::vector<int> queue{u};
+      int found = -1;
+      for (size_t qi = 0; qi < queue.size() && found < 0; ++qi) {
+        const int t = queue[qi];
+        for (int q = 0; q < 64 && found < 0; ++q) {
+          if (taken[q] || tr[q] != t || seen[hr[q]]) continue;
+          seen[hr[q]] = true;
+          prev_edge[hr[q]] = q;
+          if (match_h[hr[q]] < 0) found = hr[q];
+          else queue.push_back(tr[match_h[hr[q]]]);
+        }
+      }
+      // a regular bipartite graph always has a perfect matching, so the path exists
+      if (found < 0) return false;
+      for (int h = found; h >= 0;) {
+        const int q = prev_edge[h];
+        const int t = tr[q];
+        const int next = match_t[t] >= 0 ? hr[match_t[t]] : -1;
+        match_h[h] = q;
+        match_t[t] = q;
+        h = (t == u) ? -1 : next;
+      }
     }
+    for (int r = 0; r < 16; ++r) { taken[match_t[r]] = true; block[match_t[r]] = b; }
   }
-  int n0 = 0, n1 = 32;
-  for (int q = 0; q < 64; ++q) lane_of[q] = color[q] == 0 ? n0++ : n1++;
+  // halves of each block: alternate colours along tail-mate / head-mate cycles
+  for (int b = 0; b < 4; ++b) {
+    int by_t[16], by_h[16];
+    for (int q = 0; q < 64; ++q)
+      if (block[q] == b) { by_t[tr[q]] = q; by_h[hr[q]] = q; }
+    int color[64];
+    for (int q = 0; q < 64; ++q) color[q] = -1;
+    int n[2] = {0, 0};
+    for (int r0 = 0; r0 < 16; ++r0) {
+      int q = by_t[r0];
+      if (color[q] >= 0) continue;
+      int c = 0;
+      bool via_tail = true;
+      while (color[q] < 0) {
+        color[q] = c;
+        lane_of[q] = 16 * b + 8 * c + n[c]++;
+        q = via_tail ? by_t[tr[q] ^ 8] : by_h[hr[q] ^ 8];
+        via_tail = !via_tail;
+        c ^= 1;
+      }
+    }
+    if (n[0] != 8 || n[1] != 8) return false;
+  }
+  return true;
 }
 
 }  // namespace pq
@@ -184,7 +235,8 @@ int pq_build_records(const int16_t* pairs_h, const uint16_t* theta_h, int K, voi
         c16[q] = f16_from_double(std::cos(th));
         s16[q] = f16_from_double(std::sin(th));
       }
-      order_layer(pi, pj, tail, head, lane_of);
+      if (!order_layer(pi, pj, tail, head, lane_of))
+        return set_error(PQ_ERR_RECORDS, "pairs layer %d group %d: lane ordering failed", r, g);
       for (int q = 0; q < 64; ++q) {
         // listing the pair as (j, i) is the same rotation with sin negated
         const uint16_t s = (tail[q] == pi[q]) ? s16[q] : static_cast<uint16_t>(s16[q] ^ 0x8000);

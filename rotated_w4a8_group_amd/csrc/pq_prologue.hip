@@ -9,12 +9,20 @@
 // This translation unit is compiled with -ffp-contract=off: every multiply and add in the
 // rotation rounds separately in binary32, which is the arithmetic the results are defined by.
 //
-// Launch shape: one 256-thread workgroup (4 waves) per (partition, group, token chunk). The
-// workgroup stages the 512 records of its (partition, group) in LDS once; each wave then keeps
-// its lane's 8 records in registers and processes TOK tokens at a time. A token-group lives
-// in the wave as 2 channels per lane; the layers update a 512-byte LDS copy of it in place.
-// Record lane order (pq_build_records) makes every one of those reads and writes free of bank
-// conflicts. amax and the row-sum are wave reductions.
+// Launch shape: every wave is an independent unit of work, one (partition, group, token chunk);
+// a 256-thread workgroup holds 4 of them and never synchronises. A wave keeps its lane's 8
+// rotation records in registers and carries 8 tokens per step as two quads of 4: lane
+// (t = lane/16, c = lane%16) loads 16 bytes (channels 8c..8c+7) of token t of each quad, the
+// next step's loads in flight while the current step computes. The scaled values go to LDS
+// token-minor, channel ch of a quad in the 16-byte row ch + ch/8 (4 tokens), so the layer
+// updates are one 16-byte read and write per pair end and 4 tokens per lane; the record lane
+// order (pq_build_records) keeps those accesses and the transposing scalar ones free of bank
+// conflicts. amax and the row-sum are reductions over the 16 lanes of a token (DPP).
+//
+// Encoding: fl32(v * inv) + 0 (which turns -0 into +0) goes straight to the hardware convert.
+// For |v| <= amax and a finite inv this equals the saturating encoder unless the convert meets
+// a NaN or a value past the e4m3 range, and then it writes a NaN code (0x7F/0xFF). A wave that
+// finds such a code, or a non-finite inv, re-encodes its two quads with the full encoder.
 #include "pq_device.h"
 #include "pq_internal.h"
 
@@ -22,114 +30,218 @@
 
 namespace pq {
 
-constexpr int kProWaves = 4;
-constexpr int kProTok = 4;  // tokens a wave rotates concurrently
+constexpr int kProWaves = 4;                 // waves per workgroup (independent units)
+constexpr int kProQuads = 2;                 // token quads per wave step
+constexpr int kProStep = 4 * kProQuads;      // tokens per wave step
+constexpr int kProQuadBytes = 144 * 16;      // 128 channel rows + 15 pad rows, 16 B each
+constexpr int kProUnits = 8192;              // aim for about this many wave units
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+__device__ __forceinline__ uint32_t lds_row_bytes(uint32_t ch) { return (ch + (ch >> 3)) << 4; }
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+// Reductions over the 16 lanes of a DPP row: swap within pairs, within quads, mirror the
+// 8-lane halves, mirror the row. Every lane of the row ends with the result.
+__device__ __forceinline__ float row_max(float v) {
+  v = __builtin_fmaxf(v, __builtin_bit_cast(float, dpp<0xB1>(__builtin_bit_cast(int, v))));
+  v = __builtin_fmaxf(v, __builtin_bit_cast(float, dpp<0x4E>(__builtin_bit_cast(int, v))));
+  v = __builtin_fmaxf(v, __builtin_bit_cast(float, dpp<0x141>(__builtin_bit_cast(int, v))));
+  v = __builtin_fmaxf(v, __builtin_bit_cast(float, dpp<0x140>(__builtin_bit_cast(int, v))));
   return v;
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+__device__ __forceinline__ int row_sum(int v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
   return v;
 }
 
 __device__ __forceinline__ float recip_rn(float a) { return 1.0f / a; }
 
+// Nonzero when a byte of w is 0x7F or 0xFF (an E4M3FN NaN code).
+__device__ __forceinline__ uint32_t nan_bytes(uint32_t w) {
+  return ((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+}
+
+// fl32 sum of the 8 decoded codes in w0 (low channels) and w1, times 512: an exact integer.
+__device__ __forceinline__ int code_units(uint32_t w0, uint32_t w1) {
+  float s = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const auto d0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(h ? w1 : w0), false);
+    const auto d1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(h ? w1 : w0), true);
+    s = s + d0[0] + d0[1] + d1[0] + d1[1];
+  }
+  // each decoded code is k * 2^-9 with |k| <= 229376, so 8 of them sum exactly in binary32
+  return static_cast<int>(s * 512.0f);
+}
+
+__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) { return f16_to_f32(w); }
+__device__ __forceinline__ float half_hi(uint32_t w) { return f16_to_f32(w >> 16); }
+
+template <bool kVec16>
+__device__ __forceinline__ uint4 load_x8(const uint16_t* p) {
+  if constexpr (kVec16) {
+    return *reinterpret_cast<const uint4*>(p);
+  } else {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    return make_uint4(q[0], q[1], q[2], q[3]);
+  }
+}
+
+template <bool kVec16>
 __global__ __launch_bounds__(256) void rotate_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int K, int P,
     const uint2* __restrict__ rec, const uint16_t* __restrict__ cs, uint8_t* __restrict__ A,
-    float* __restrict__ ASG, float* __restrict__ RS, int tok_per_block) {
+    float* __restrict__ ASG, float* __restrict__ RS, int tok, int chunks) {
+  __shared__ __align__(16) uint8_t sbuf[kProWaves][kProQuads * kProQuadBytes];
+
   const int G = K >> 7;
-  int bid = blockIdx.x;
-  const int p = bid % P;
-  bid /= P;
-  const int g = bid % G;
-  const int chunk = bid / G;
-
-  __shared__ uint2 srec[PQ_LAYERS * 64];
-  __shared__ float sbuf[kProWaves][kProTok][128];
-
-  const int half = K >> 1;
-  for (int t = threadIdx.x; t < PQ_LAYERS * 64; t += blockDim.x) {
-    const int r = t >> 6, l = t & 63;
-    srec[t] = rec[(static_cast<size_t>(p) * PQ_LAYERS + r) * half + g * 64 + l];
-  }
-  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x * kProWaves + wave;
+  if (unit >= chunks * G * P) return;
+  const int g = unit % G;
+  const int chunk = (unit / G) % chunks;
+  const int p = unit / (G * chunks);
+  const int m0 = chunk * tok;
+  const int m_end = min(M, m0 + tok);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int t = lane >> 4, c = lane & 15;
+  const int half = K >> 1;
+
+  uint32_t ta[PQ_LAYERS], ha[PQ_LAYERS];
   float cr[PQ_LAYERS], sr[PQ_LAYERS];
-  uint32_t ti[PQ_LAYERS], hi[PQ_LAYERS];
 #pragma unroll
   for (int r = 0; r < PQ_LAYERS; ++r) {
-    const uint2 q = srec[r * 64 + lane];
-    ti[r] = q.x & 0x7Fu;           // channel indices are 0..127
-    hi[r] = (q.x >> 8) & 0x7Fu;
+    const uint2 q = rec[(static_cast<size_t>(p) * PQ_LAYERS + r) * half + g * 64 + lane];
+    ta[r] = lds_row_bytes(q.x & 0x7Fu);   // channel indices are 0..127
+    ha[r] = lds_row_bytes((q.x >> 8) & 0x7Fu);
     cr[r] = f16_to_f32(q.y);
     sr[r] = f16_to_f32(q.y >> 16);
   }
-  const uint32_t csw = *reinterpret_cast<const uint32_t*>(cs + static_cast<size_t>(p) * K + g * 128 + 2 * lane);
-  const float cs0 = f16_to_f32(csw), cs1 = f16_to_f32(csw >> 16);
+  const uint32_t* csp = reinterpret_cast<const uint32_t*>(cs + static_cast<size_t>(p) * K + g * 128 + 8 * c);
+  const uint32_t cw[4] = {csp[0], csp[1], csp[2], csp[3]};
 
-  float* buf = &sbuf[wave][0][0];
-  const int m_begin = chunk * tok_per_block;
-  const int m_end = min(M, m_begin + tok_per_block);
+  uint8_t* const buf = sbuf[wave];
+  // this lane's scalar slot in a quad: channel 8c+j of token t at row 9c+j, dword t
+  uint8_t* const slot = buf + (9 * c) * 16 + 4 * t;
+  const uint16_t* const xg = x + g * 128 + 8 * c;
   const size_t out_base = static_cast<size_t>(p) * M;
 
-  for (int mb = m_begin + wave * kProTok; mb < m_end; mb += kProWaves * kProTok) {
-    uint32_t xw[kProTok];
+  auto load_step = [&](int mb, uint4 (&dst)[kProQuads]) {
 #pragma unroll
-    for (int t = 0; t < kProTok; ++t) {
-      const int m = mb + t;
-      xw[t] = (m < m_end) ? *reinterpret_cast<const uint32_t*>(x + static_cast<size_t>(m) * ldx + g * 128 + 2 * lane) : 0u;
+    for (int q = 0; q < kProQuads; ++q) {
+      const int m = min(mb + 4 * q + t, m_end - 1);   // clamped: always a valid row
+      dst[q] = load_x8<kVec16>(xg + static_cast<size_t>(m) * ldx);
     }
+  };
+
+  auto run_step = [&](int mb, const uint4 (&xs)[kProQuads]) {
+    // v = x * cs (exact: 11 x 11 significand bits), transposed into token-minor rows
 #pragma unroll
-    for (int t = 0; t < kProTok; ++t) {
-      float2 v;
-      v.x = f16_to_f32(xw[t]) * cs0;       // exact: 11 x 11 significand bits
-      v.y = f16_to_f32(xw[t] >> 16) * cs1;
-      *reinterpret_cast<float2*>(buf + t * 128 + 2 * lane) = v;
+    for (int q = 0; q < kProQuads; ++q) {
+      const uint32_t xw[4] = {xs[q].x, xs[q].y, xs[q].z, xs[q].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<float*>(slot + q * kProQuadBytes + (2 * i) * 16) = half_lo(xw[i]) * half_lo(cw[i]);
+        *reinterpret_cast<float*>(slot + q * kProQuadBytes + (2 * i + 1) * 16) = half_hi(xw[i]) * half_hi(cw[i]);
+      }
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int r = 0; r < PQ_LAYERS; ++r) {
-      float a[kProTok], b[kProTok];
+      float4 a[kProQuads], b[kProQuads];
 #pragma unroll
-      for (int t = 0; t < kProTok; ++t) {
-        a[t] = buf[t * 128 + ti[r]];
-        b[t] = buf[t * 128 + hi[r]];
+      for (int q = 0; q < kProQuads; ++q) {
+        a[q] = *reinterpret_cast<const float4*>(buf + q * kProQuadBytes + ta[r]);
+        b[q] = *reinterpret_cast<const float4*>(buf + q * kProQuadBytes + ha[r]);
       }
 #pragma unroll
-      for (int t = 0; t < kProTok; ++t) {
-        const float ca = cr[r] * a[t], sb = sr[r] * b[t];
-        const float cb = cr[r] * b[t], sa = sr[r] * a[t];
-        buf[t * 128 + ti[r]] = ca + sb;
-        buf[t * 128 + hi[r]] = cb - sa;
+      for (int q = 0; q < kProQuads; ++q) {
+        const float av[4] = {a[q].x, a[q].y, a[q].z, a[q].w};
+        const float bv[4] = {b[q].x, b[q].y, b[q].z, b[q].w};
+        float na[4], nb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float ca = cr[r] * av[k], sb = sr[r] * bv[k];
+          const float cb = cr[r] * bv[k], sa = sr[r] * av[k];
+          na[k] = ca + sb;
+          nb[k] = cb - sa;
+        }
+        *reinterpret_cast<float4*>(buf + q * kProQuadBytes + ta[r]) = make_float4(na[0], na[1], na[2], na[3]);
+        *reinterpret_cast<float4*>(buf + q * kProQuadBytes + ha[r]) = make_float4(nb[0], nb[1], nb[2], nb[3]);
       }
       __builtin_amdgcn_wave_barrier();
     }
+    float v[kProQuads][8], inv[kProQuads], asg[kProQuads];
+    uint32_t w[kProQuads][2];
+    uint32_t bad = 0;
 #pragma unroll
-    for (int t = 0; t < kProTok; ++t) {
-      const int m = mb + t;
-      const float2 v = *reinterpret_cast<const float2*>(buf + t * 128 + 2 * lane);
-      const float amax = wave_max(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)));
-      const float asg = amax * 0x1.24924ap-9f;   // fl32(1/448) = 0x3B124925
-      const float inv = recip_rn(asg);             // 1/0 = inf -> 0*inf = NaN -> code 0
-      const uint32_t codes = e4m3_encode2(v.x * inv, v.y * inv);
-      const int units = wave_sum(e4m3_units(codes & 0xFFu) + e4m3_units(codes >> 8));
+    for (int q = 0; q < kProQuads; ++q) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[q][j] = *reinterpret_cast<const float*>(slot + q * kProQuadBytes + j * 16);
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < kProQuads; ++q) {
+      float m = __builtin_fabsf(v[q][0]);
+#pragma unroll
+      for (int j = 1; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[q][j]));
+      const float amax = row_max(m);
+      asg[q] = amax * 0x1.24924ap-9f;   // fl32(1/448) = 0x3B124925
+      inv[q] = recip_rn(asg[q]);
+      float s[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s[j] = v[q][j] * inv[q] + 0.0f;
+      w[q][0] = pack4(s[0], s[1], s[2], s[3]);
+      w[q][1] = pack4(s[4], s[5], s[6], s[7]);
+      bad |= nan_bytes(w[q][0]) | nan_bytes(w[q][1]);
+      bad |= (__builtin_fabsf(inv[q]) == __builtin_inff()) ? 1u : 0u;
+    }
+    if (__builtin_amdgcn_ballot_w64(bad != 0)) {
+      // rare: a NaN or out-of-range value somewhere in the wave; take the full encoder
+#pragma unroll
+      for (int q = 0; q < kProQuads; ++q) {
+        w[q][0] = e4m3_encode2(v[q][0] * inv[q], v[q][1] * inv[q]) |
+                  (e4m3_encode2(v[q][2] * inv[q], v[q][3] * inv[q]) << 16);
+        w[q][1] = e4m3_encode2(v[q][4] * inv[q], v[q][5] * inv[q]) |
+                  (e4m3_encode2(v[q][6] * inv[q], v[q][7] * inv[q]) << 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kProQuads; ++q) {
+      const int units = row_sum(code_units(w[q][0], w[q][1]));
+      const int m = mb + 4 * q + t;
       if (m < m_end) {
-        *reinterpret_cast<uint16_t*>(A + (out_base + m) * K + g * 128 + 2 * lane) = static_cast<uint16_t>(codes);
-        if (lane == 0) {
-          ASG[(out_base + m) * G + g] = asg;
+        *reinterpret_cast<uint2*>(A + (out_base + m) * K + g * 128 + 8 * c) = make_uint2(w[q][0], w[q][1]);
+        if (c == 0) {
+          ASG[(out_base + m) * G + g] = asg[q];
           RS[(out_base + m) * G + g] = static_cast<float>(units) * 0x1p-9f;
         }
       }
     }
-    __builtin_amdgcn_wave_barrier();
+  };
+
+  uint4 xa[kProQuads], xb[kProQuads];
+  load_step(m0, xa);
+  for (int mb = m0;; mb += 2 * kProStep) {
+    load_step(mb + kProStep, xb);
+    run_step(mb, xa);
+    if (mb + kProStep >= m_end) break;
+    load_step(mb + 2 * kProStep, xa);
+    run_step(mb + kProStep, xb);
+    if (mb + 2 * kProStep >= m_end) break;
   }
 }
 
@@ -172,15 +284,21 @@ int pq_rotate_quant(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const
   if (!aligned(x_d, 4) || !aligned(rec_d, 8) || !aligned(cs_d, 4) || !aligned(a_d, 16) || !aligned(asg_d, 4) || !aligned(rs_d, 4))
     return set_error(PQ_ERR_ALIGN, "pq_rotate_quant: misaligned pointer");
   const int G = K / PQ_GROUP;
-  // tokens per workgroup: aim for >= ~2048 workgroups, 16..256 tokens each
-  const int64_t want = (static_cast<int64_t>(M) * G * P + 2047) / 2048;
-  int tok = static_cast<int>(std::min<int64_t>(256, std::max<int64_t>(16, (want + 15) / 16 * 16)));
+  // tokens per wave unit: a multiple of the 8-token step, as few as keep the unit count near
+  // kProUnits (short units for small M, at most 256 tokens)
+  const int64_t rows = static_cast<int64_t>(G) * P;
+  const int64_t want = (static_cast<int64_t>(M) * rows + kProUnits - 1) / kProUnits;
+  const int tok = static_cast<int>(std::min<int64_t>(256, std::max<int64_t>(kProStep, (want + kProStep - 1) / kProStep * kProStep)));
   const int64_t chunks = (M + tok - 1) / tok;
-  const int64_t blocks = chunks * G * P;
-  if (blocks > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "pq_rotate_quant: problem too large");
-  hipLaunchKernelGGL(rotate_quant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+  const int64_t units = chunks * rows;
+  const int64_t blocks = (units + kProWaves - 1) / kProWaves;
+  if (units > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "pq_rotate_quant: problem too large");
+  const bool vec16 = aligned(x_d, 16) && (ldx % 8) == 0;
+  auto kern = vec16 ? rotate_quant_kernel<true> : rotate_quant_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), x_d, ldx, M, K, P,
-                     static_cast<const uint2*>(rec_d), cs_d, a_d, asg_d, rs_d, tok);
+                     static_cast<const uint2*>(rec_d), cs_d, a_d, asg_d, rs_d, tok,
+                     static_cast<int>(chunks));
   return launch_status("pq_rotate_quant");
 }
 

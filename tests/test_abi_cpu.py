@@ -66,18 +66,72 @@ def test_records_match_oracle_up_to_lane_order(wl_name):
                 assert a == b, (r, g)
 
 
+def _lds_row(ch):
+    return ch + (ch >> 3)
+
+
+def _check_lane_order(lib):
+    """In the prologue a quad of tokens keeps channel ch in the 16-byte LDS row ch + ch//8 and
+    lane l reads and writes the rows of its record's two channels. 16-byte accesses are served
+    16 lanes (64 banks) or 8 lanes (32 banks) at a time, so the rows must be distinct mod 16
+    in every 16-lane block and mod 8 in every 8-lane half-block, for the first channels and for
+    the second channels separately."""
+    ij = lib[..., :4].copy().view(np.uint32)[..., 0]
+    for r in range(ij.shape[0]):
+        for g in range(ij.shape[1] // 64):
+            w = ij[r, 64 * g:64 * g + 64].astype(int)
+            for col in (w & 0xFF, (w >> 8) & 0xFF):
+                row = _lds_row(col)
+                for blk in range(4):
+                    assert len(set(row[16 * blk:16 * blk + 16] % 16)) == 16, (r, g, blk)
+                for hb in range(8):
+                    assert len(set(row[8 * hb:8 * hb + 8] % 8)) == 8, (r, g, hb)
+
+
 def test_records_lane_order_is_bank_conflict_free():
     wl = synth.WORKLOADS["qkv"]
     pl, tl, _ = synth.rotations(wl)
-    lib = pq.build_records(pl[1][:, :2048], tl[1][:, :1024])
-    ij = lib[..., :4].copy().view(np.uint32)[..., 0]
+    _check_lane_order(pq.build_records(pl[1][:, :2048], tl[1][:, :1024]))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_records_lane_order_any_pairing(seed):
+    """Any pairing of each group's channels orders conflict-free, including adversarial ones
+    (every pair inside one 8-channel block, pairs with equal rows mod 16, identity pairing)."""
+    rng = np.random.default_rng(seed)
+    K = 128 * 8
+    pairs = np.empty((8, K), np.int16)
     for r in range(8):
-        for g in range(16):
-            t = (ij[r, 64 * g:64 * g + 64] & 0xFF).astype(int)
-            h = ((ij[r, 64 * g:64 * g + 64] >> 8) & 0xFF).astype(int)
-            assert len(set(t % 64)) == 64 and len(set(h % 64)) == 64
-            for half in (slice(0, 32), slice(32, 64)):
-                assert len(set(t[half] % 32)) == 32 and len(set(h[half] % 32)) == 32
+        for g in range(K // 128):
+            kind = (r + g + seed) % 4
+            if kind == 0:
+                perm = rng.permutation(128)
+            elif kind == 1:
+                perm = np.arange(128)                      # (0,1), (2,3), ...: same 8-block
+            elif kind == 2:
+                # pair ch with the channel whose row is 16 higher: equal rows mod 16
+                order = sorted(range(128), key=lambda ch: (_lds_row(ch) % 16, ch))
+                perm = np.array(order)
+            else:
+                perm = np.concatenate([np.arange(0, 128, 2), np.arange(1, 128, 2)])
+                perm = perm.reshape(2, 64).T.reshape(-1)  # (0,1),(2,3) interleaved differently
+                perm = rng.permutation(perm.reshape(64, 2)).reshape(-1)
+            pairs[r, 128 * g:128 * g + 128] = perm
+    theta = rng.standard_normal((8, K // 2)).astype(np.float16)
+    lib = pq.build_records(pairs, theta)
+    _check_lane_order(lib)
+    # and the records still hold exactly the given rotations
+    ij = lib[..., :4].copy().view(np.uint32)[..., 0]
+    ref = orec.build(pairs, theta)
+    lc = lib[..., 4:6].copy().view(np.uint16)[..., 0]
+    ls = lib[..., 6:8].copy().view(np.uint16)[..., 0]
+    for r in range(8):
+        for g in range(K // 128):
+            sl = slice(64 * g, 64 * g + 64)
+            a = sorted(_canon(*t) for t in zip(ij[r, sl] & 0xFF, (ij[r, sl] >> 8) & 0xFF, lc[r, sl], ls[r, sl]))
+            b = sorted(_canon(*t) for t in zip(ref["i"][r, sl], ref["j"][r, sl],
+                                               ref["cos16"][r, sl], ref["sin16"][r, sl]))
+            assert a == b, (r, g)
 
 
 def test_records_reject_bad_pairs():

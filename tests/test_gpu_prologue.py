@@ -66,6 +66,14 @@ def test_prologue_edge_cases():
     A2, S2, R2 = pq.rotate_quant(xs, to_dev(records_for(pl, tl)), to_dev(np.stack(cl)))
     assert torch.equal(A2, A) and torch.equal(S2.view(torch.int32), S.view(torch.int32))
     assert torch.equal(R2.view(torch.int32), R.view(torch.int32))
+    # x rows that are only 4-byte aligned: ldx = K + 2, and a view starting 2 columns in
+    for pad, start in ((2, 0), (6, 2)):
+        wide = np.zeros((wl.M, wl.K + pad), dtype=np.float16)
+        wide[:, start:start + wl.K] = x
+        xs = to_dev(wide)[:, start:start + wl.K]
+        A3, S3, R3 = pq.rotate_quant(xs, to_dev(records_for(pl, tl)), to_dev(np.stack(cl)))
+        assert torch.equal(A3, A) and torch.equal(S3.view(torch.int32), S.view(torch.int32))
+        assert torch.equal(R3.view(torch.int32), R.view(torch.int32))
     # K = 128, one token
     wl1 = synth.Workload("edge1", 41, 1, 128, 16)
     x1 = synth.activations(wl1)
