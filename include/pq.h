@@ -126,8 +126,9 @@ int pq_rotate_quant(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const
  * y_d             out bf16 [M, ldy], ldy >= N, 4-byte aligned, ldy even.
  * ws_d, ws_bytes  device workspace of at least pq_gemm_workspace_bytes(M, N, K) bytes, 16-byte
  *                 aligned (may be NULL when that is 0: M <= 16). For M > 16 the call first
- *                 writes the activation operand of the zero-point epilogue there (sized for up
- *                 to 3 partitions); its contents need no initialisation and are not kept.
+ *                 writes the activation operand of the zero-point epilogue and a transposed
+ *                 copy of asg there (sized for up to 3 partitions); its contents need no
+ *                 initialisation and are not kept.
  * Requires K % 128 == 0, N % 16 == 0.
  */
 size_t pq_gemm_workspace_bytes(int M, int N, int K);

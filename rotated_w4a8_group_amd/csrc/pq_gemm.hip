@@ -142,7 +142,7 @@ __global__ void pack_zpe_kernel(const uint32_t* __restrict__ sz, int G, int N, u
 // for partition p, 16-row tile mt and chunk c, 1 KiB where lane l (row 16mt + l%16) holds the
 // 8 bf16 at k' = 32c + 8(l/16) + 0..7 of -[a1 | a1 | a2], ar = asg * rs = a1 + a2 (bf16 pieces).
 __global__ void zpe_act_kernel(const float* __restrict__ ASG, const float* __restrict__ RS, int M, int G,
-                               int P, u32x4* __restrict__ zpa) {
+                               int P, u32x4* __restrict__ zpa, float* __restrict__ asgt) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int KC = zpe_chunks(G), MT = (M + 15) / 16;
   if (idx >= static_cast<int64_t>(P) * MT * KC * 64) return;
@@ -162,6 +162,7 @@ __global__ void zpe_act_kernel(const float* __restrict__ ASG, const float* __res
       const int piece = kp / G, g = kp % G;
       const size_t o = (static_cast<size_t>(p) * M + row) * G + g;
       const float ar = ASG[o] * RS[o];
+      if (piece == 0) asgt[(static_cast<size_t>(p) * G + g) * M + row] = ASG[o];   // [P][G][M] copy
       const uint32_t a1 = f32_to_bf16(ar);
       v = ((piece == 2) ? f32_to_bf16(ar - bf16_to_f32(a1)) : a1) ^ 0x8000u;   // negated
     }
@@ -172,6 +173,12 @@ __global__ void zpe_act_kernel(const float* __restrict__ ASG, const float* __res
 
 size_t zpe_act_bytes(int M, int G, int P) {
   return static_cast<size_t>(P) * ((M + 15) / 16) * zpe_chunks(G) * 1024;
+}
+
+// The group scales transposed to [P][G][M] (f32), so that a tile's scales of one group are
+// contiguous for the direct loads.
+size_t asgt_bytes(int M, int G, int P) {
+  return (static_cast<size_t>(P) * G * M * 4 + 255) / 256 * 256;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -400,8 +407,10 @@ int decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
 // ---------------------------------------------------------------------------------------
 // prefill (M > 16). One 512-thread workgroup (8 waves) per output tile of TM x TN; the waves
 // form a WM x WN grid of (TM/WM) x (TN/WN) blocks; one 128-group per k-step. Operands move
-// global -> LDS by direct LDS loads through a 3-stage ring (2 groups ahead); the LDS images are
-// in matrix-core fragment order so every lane reads 16 contiguous bytes. Per group and wave the
+// global -> LDS by direct LDS loads through a 3-stage ring (2 groups ahead). The activation slab
+// arrives as whole 128-byte rows (8 rows per load, fully used cache lines) with the 16-byte chunk
+// index XOR-swizzled by (row/2)%8, which keeps the fragment reads free of bank conflicts; the
+// weight image is already in fragment order (each lane reads 16 contiguous bytes). Per group and wave the
 // products T = MFMA(A_g, codes_g) are folded as acc += (asg * 512 sc) * T (2 VALU per output),
 // each row fragment's products issued before the previous fragment's fold. After the loop the
 // zero-point term is subtracted as a bf16 matrix-core product (pack_zpe_kernel / zpe_act_kernel
@@ -418,14 +427,14 @@ constexpr int kPfLds = kPfStages * 51200;   // the 256x256 ring (the largest)
 template <int TM, int TN, int WM, int WN>
 struct PfTile {
   static constexpr int MF = TM / WM / 16, NF = TN / WN / 16;   // fragments per wave
-  static constexpr int kOffA = 0;                              // [TM/16][2 halves][64 lanes][16 B]
+  static constexpr int kOffA = 0;                              // [TM rows][8 chunks][16 B], chunks swizzled
   static constexpr int kOffB = TM * 128;                       // [TN/16 tiles][64 lanes][16 B]
   static constexpr int kOffAsg = kOffB + TN * 64;              // [TM] f32
   static constexpr int kOffSz = kOffAsg + TM * 4;              // [TN] u32
   static constexpr int kStage = (kOffSz + TN * 4 + 255) / 256 * 256;
   static constexpr int nA = TM / 8, nB = TN / 16, nAs = TM / 64, nSz = TN / 64;
   static constexpr int nD = nA + nB + nAs + nSz;                // direct loads per group
-  static constexpr int kPerWave = (nD + kPfWaves - 1) / kPfWaves;
+  static constexpr int kPerWave = (nD + 3) / 4;                 // loads per wave of the issuing half
   static constexpr int kOutStride = TN + 8;                    // bf16 per staged output row
   static_assert(WM * WN == kPfWaves && MF >= 1 && NF >= 1 && TM % 64 == 0 && TN % 64 == 0, "tile");
   static_assert(kPfStages * kStage <= kPfLds && TM * kOutStride * 2 <= kPfLds, "LDS");
@@ -474,7 +483,7 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
 
 template <int TM, int TN, int WM, int WN>
 __device__ __forceinline__ void prefill_tile(
-    const uint8_t* __restrict__ A, const float* __restrict__ ASG, int M, int K,
+    const uint8_t* __restrict__ A, const float* __restrict__ ASGT, int M, int K,
     const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe, const u32x4* __restrict__ zpa,
     const uint32_t* __restrict__ sz, int N, int p, int m0, int n0, uint16_t* __restrict__ y,
     int64_t ldy, bool vec16, uint8_t* smem) {
@@ -486,11 +495,14 @@ __device__ __forceinline__ void prefill_tile(
   const int wm = wave / WN, wn = wave % WN;
   const int col = lane & 15, kq = lane >> 4;
   const int last_tile = N / 16 - 1;
-  const float* asgp = ASG + static_cast<size_t>(p) * M * G;
+  const float* asgp = ASGT + static_cast<size_t>(p) * G * M;   // [G][M] for this partition
 
-  // This wave's share of the group's direct loads: entry d = wave + 8 i of the tile's list (A
-  // half-fragments, weight tiles, asg rows, SZ columns), taken modulo the list length so every
-  // wave issues PW loads (a repeated entry writes the same bytes again). Each entry is a scalar
+  // The direct loads of a group are issued by one half of the workgroup, waves 0-3 for even
+  // groups and waves 4-7 for odd ones (one wave per SIMD each), so that on every SIMD one wave
+  // computes while its partner is held up issuing loads. This wave's share: entry
+  // d = (wave % 4) + 4 i of the tile's list (A half-fragments, weight tiles, asg rows, SZ
+  // columns), taken modulo the list length so every wave of a half issues PW loads (a repeated
+  // entry writes the same bytes again). Each entry is a scalar
   // base (advanced per group on the scalar unit) plus a fixed 32-bit lane offset. Rows past M
   // and column tiles past N are clamped to valid memory; their results are never stored.
   const uint8_t* sbase[PW];
@@ -501,12 +513,12 @@ __device__ __forceinline__ void prefill_tile(
   const uint8_t* Ap = A + static_cast<size_t>(p) * M * K;
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
-    const int d = (wave + kPfWaves * i) % TL::nD;
+    const int d = ((wave & 3) + 4 * i) % TL::nD;
     if (d < TL::nA) {
-      const int mf = d >> 1, h = d & 1;
-      const int row = min(m0 + 16 * mf + (lane & 15), M - 1);
+      const int r = 8 * d + (lane >> 3);                 // tile row; lane%8 = chunk slot
+      const int row = min(m0 + r, M - 1);
       sbase[i] = Ap;
-      voff[i] = static_cast<uint32_t>(row * K + 32 * (lane >> 4) + 16 * h);
+      voff[i] = static_cast<uint32_t>(row * K + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
       step[i] = 128; dst[i] = TL::kOffA + d * 1024; wide[i] = true;
     } else if (d < TL::nA + TL::nB) {
       const int j = d - TL::nA;
@@ -517,8 +529,8 @@ __device__ __forceinline__ void prefill_tile(
     } else if (d < TL::nA + TL::nB + TL::nAs) {
       const int j = d - TL::nA - TL::nB;
       sbase[i] = reinterpret_cast<const uint8_t*>(asgp);
-      voff[i] = static_cast<uint32_t>(min(m0 + 64 * j + lane, M - 1) * G * 4);
-      step[i] = 4; dst[i] = TL::kOffAsg + j * 256; wide[i] = false;
+      voff[i] = static_cast<uint32_t>(min(m0 + 64 * j + lane, M - 1) * 4);
+      step[i] = static_cast<size_t>(M) * 4; dst[i] = TL::kOffAsg + j * 256; wide[i] = false;
     } else {
       const int j = d - TL::nA - TL::nB - TL::nAs;
       sbase[i] = reinterpret_cast<const uint8_t*>(sz);
@@ -542,15 +554,17 @@ __device__ __forceinline__ void prefill_tile(
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
-  if (G > 1) issue(1, 1);
+  const int half = wave >> 2;
+  if (half == 0) issue(0, 0);
+  if (G > 1 && half == 1) issue(1, 1);
   for (int g = 0; g < G; ++g) {
-    // This wave's loads for group g have landed once at most the PW loads of group g+1 are
-    // outstanding; the barrier then makes every wave's group-g data visible and guarantees no
-    // wave still reads stage (g+2)%3. (__syncthreads would also drain the group g+1 loads.)
-    if (g + 1 < G) wait_vm_lgkm_barrier<PW>();
-    else wait_vm_lgkm_barrier<0>();
-    if (g + 2 < G) issue((g + 2) % kPfStages, g + 2);
+    // Group g was loaded by half g%2, whose only outstanding loads are group g's: it waits for
+    // all of them. The other half's outstanding loads (at most PW, group g+1) need not land. The
+    // barrier then makes group g visible to every wave and guarantees that no wave still reads
+    // stage (g+2)%3. (__syncthreads would also drain the group g+1 loads.)
+    if ((g & 1) == half) wait_vm_lgkm_barrier<0>();
+    else wait_vm_lgkm_barrier<PW>();
+    if (g + 2 < G && (g & 1) == half) issue((g + 2) % kPfStages, g + 2);
     const uint8_t* st = smem + (g % kPfStages) * TL::kStage;
 
     v8i bf[NF];
@@ -560,15 +574,18 @@ __device__ __forceinline__ void prefill_tile(
       bf[nf] = unpack_codes(*reinterpret_cast<const u32x4*>(st + TL::kOffB + (wn * NF + nf) * 1024 + lane * 16));
       s9[nf] = f16_to_f32(*reinterpret_cast<const uint32_t*>(st + TL::kOffSz + (wn * NF * 16 + 16 * nf + col) * 4)) * 512.0f;
     }
+    // fragment lane l: row l%16 of the 16-row block, k chunks 2(l/16) and 2(l/16)+1, swizzled
+    const int arow = lane & 15, ac0 = 2 * (lane >> 4), asw = arow >> 1;
+    const int aoff0 = arow * 128 + 16 * (ac0 ^ asw), aoff1 = arow * 128 + 16 * ((ac0 + 1) ^ asw);
     // the products of row fragment mf are issued before the fold of mf-1
     v4f Tb[2][NF];
     float4 asb[2];
 #pragma unroll
     for (int mf = 0; mf <= MF; ++mf) {
       if (mf < MF) {
-        const uint8_t* ap = st + TL::kOffA + ((wm * MF + mf) * 2) * 1024 + lane * 16;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 1024);
+        const uint8_t* ap = st + TL::kOffA + (wm * MF + mf) * 2048;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap + aoff0);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + aoff1);
         const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
         asb[mf & 1] = *reinterpret_cast<const float4*>(st + TL::kOffAsg + (wm * MF * 16 + 16 * mf + 4 * kq) * 4);
 #pragma unroll
@@ -648,7 +665,7 @@ struct PrefillMap {
 };
 
 __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ ASG, int M, int K,
+    const uint8_t* __restrict__ A, const float* __restrict__ ASGT, int M, int K,
     const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe, const u32x4* __restrict__ zpa,
     const uint32_t* __restrict__ sz, int N, int pb1, int pb2, uint16_t* __restrict__ y, int64_t ldy,
     PrefillMap map, bool vec16) {
@@ -668,13 +685,13 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
   if (m0 >= M || n0 >= N) return;   // a piece wholly past the matrix
   const int p = (n0 >= pb1) + (n0 >= pb2);
   if (map.wide) {
-    if (split == 1) prefill_tile<256, 256, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else if (split == 2) prefill_tile<128, 256, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else if (split == 4) prefill_tile<128, 128, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (split == 1) prefill_tile<256, 256, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 2) prefill_tile<128, 256, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 4) prefill_tile<128, 128, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
   } else {
-    if (split == 1) prefill_tile<128, 128, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4>(A, ASG, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (split == 1) prefill_tile<128, 128, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
   }
 }
 
@@ -756,7 +773,7 @@ int pq_pack_weights(const int32_t* qweight_d, const int32_t* qzeros_d, const uin
 size_t pq_gemm_workspace_bytes(int M, int N, int K) {
   (void)N;
   if (M <= 16 || K <= 0 || K % PQ_GROUP) return 0;     // the decode kernel needs none
-  return pq::zpe_act_bytes(M, K / PQ_GROUP, PQ_MAX_PARTITIONS);
+  return pq::zpe_act_bytes(M, K / PQ_GROUP, PQ_MAX_PARTITIONS) + pq::asgt_bytes(M, K / PQ_GROUP, PQ_MAX_PARTITIONS);
 }
 
 int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
@@ -800,13 +817,14 @@ int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, in
   const int64_t grid = static_cast<int64_t>(map.full) + static_cast<int64_t>(map.ntiles - map.full) * map.split;
   const u32x4* zpe = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(wpk_d) + static_cast<size_t>(K) * N / 2);
   u32x4* zpa = static_cast<u32x4*>(ws_d);
+  float* asgt = reinterpret_cast<float*>(static_cast<uint8_t*>(ws_d) + zpe_act_bytes(M, G, PQ_MAX_PARTITIONS));
   const int64_t zt = static_cast<int64_t>(P) * ((M + 15) / 16) * zpe_chunks(G) * 64;
   hipLaunchKernelGGL(zpe_act_kernel, dim3(static_cast<unsigned>((zt + 255) / 256)), dim3(256), 0, s,
-                     asg_d, rs_d, M, G, P, zpa);
+                     asg_d, rs_d, M, G, P, zpa, asgt);
   // 16-byte output stores need a 16-byte aligned y and a row pitch of 8 elements
   const bool vec16 = aligned(y_d, 16) && ldy % 8 == 0;
   hipLaunchKernelGGL(gemm_prefill_kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * kPfWaves), 0, s,
-                     a_d, asg_d, M, K, wpk, zpe, zpa, sz, N, pb1, pb2, y_d, ldy, map, vec16);
+                     a_d, asgt, M, K, wpk, zpe, zpa, sz, N, pb1, pb2, y_d, ldy, map, vec16);
   return launch_status("pq_gemm(prefill)");
 }
 

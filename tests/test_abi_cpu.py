@@ -177,7 +177,8 @@ def test_gemm_m0_is_noop_and_partition_ok():
     assert _gemm(M=0, P=3, N=8192, pb1=6144, pb2=7168, ldy=8192) == 0
     assert _gemm(M=0, P=2, N=256, pb1=128, ldy=256) == 0
     assert pq.gemm_workspace_bytes(8, 17408, 5120) == 0
-    assert pq.gemm_workspace_bytes(2048, 17408, 5120) == 3 * 128 * 4 * 1024
+    # zero-point operand (3 partitions x 128 row tiles x 4 chunks x 1 KiB) + transposed scales
+    assert pq.gemm_workspace_bytes(2048, 17408, 5120) == 3 * 128 * 4 * 1024 + 3 * 40 * 2048 * 4
     assert _gemm(M=32, ws=None, ws_bytes=1 << 20) == -1
 
 
