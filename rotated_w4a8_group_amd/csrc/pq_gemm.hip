@@ -414,7 +414,8 @@ int decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
 // products T = MFMA(A_g, codes_g) are folded as acc += (asg * 512 sc) * T (2 VALU per output),
 // each row fragment's products issued before the previous fragment's fold. After the loop the
 // zero-point term is subtracted as a bf16 matrix-core product (pack_zpe_kernel / zpe_act_kernel
-// operands), and the bf16 tile is staged in LDS and written as whole rows.
+// operands, staged through the idle ring), and the bf16 tile is staged in LDS and written as
+// whole rows.
 //
 // Tiles (PrefillMap): whole rounds of 256x256 tiles, one workgroup per CU; the tiles of the
 // last, partial round are cut into 2, 4 or 8 pieces (128x256, 128x128, 64x128) so that round
@@ -606,37 +607,52 @@ __device__ __forceinline__ void prefill_tile(
   }
 
   // ---- zero-point epilogue: acc += (-[a1|a1|a2]) x [z1;z2;z1] over KC chunks of 32 k'. The
-  // operands of CB chunks are requested together (a chunk index past KC re-reads the last
-  // chunk and is not used).
+  // tile's operands (TM/16 row and TN/16 column fragments, 1 KiB per fragment and chunk) move to
+  // LDS by direct loads, ZC chunks per batch into two alternating buffers of the idle ring, so
+  // each byte crosses the load path once per workgroup.
   {
-    constexpr int CB = MF >= 8 ? 2 : 4;
+    constexpr int ZC = 2;
+    constexpr int NZ = TM / 16 + TN / 16;
+    constexpr int kZBuf = NZ * ZC * 1024;
+    constexpr int ZPW = (NZ * ZC + kPfWaves - 1) / kPfWaves;
+    static_assert(2 * kZBuf <= kPfLds, "LDS");
     const int KC = zpe_chunks(G), MT = (M + 15) / 16;
-    const u32x4* zab = zpa + static_cast<size_t>(p) * MT * KC * 64 + lane;
-    for (int c0 = 0; c0 < KC; c0 += CB) {
-      u32x4 zb[CB][NF], za[CB][MF];
+    const uint8_t* zab = reinterpret_cast<const uint8_t*>(zpa) + static_cast<size_t>(p) * MT * KC * 1024;
+    const uint8_t* zwb = reinterpret_cast<const uint8_t*>(zpe);
+    auto zissue = [&](int buf, int c0) {
 #pragma unroll
-      for (int j = 0; j < CB; ++j) {
-        const int c = min(c0 + j, KC - 1);
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf) {
-          const int tt = min(n0 / 16 + wn * NF + nf, last_tile);
-          zb[j][nf] = zpe[(static_cast<size_t>(tt) * KC + c) * 64 + lane];
-        }
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf) {
-          const int mt = min(m0 / 16 + wm * MF + mf, MT - 1);
-          za[j][mf] = zab[(static_cast<size_t>(mt) * KC + c) * 64];
+      for (int i = 0; i < ZPW; ++i) {
+        const int d = wave + kPfWaves * i;                 // entry d: fragment d / ZC, chunk d % ZC
+        if (d < NZ * ZC) {
+          const int f = d / ZC, c = min(c0 + d % ZC, KC - 1);
+          const uint8_t* src = (f < TM / 16)
+              ? zab + (static_cast<size_t>(min(m0 / 16 + f, MT - 1)) * KC + c) * 1024
+              : zwb + (static_cast<size_t>(min(n0 / 16 + f - TM / 16, last_tile)) * KC + c) * 1024;
+          lds_dma16(src + lane * 16, lds0 + buf * kZBuf + d * 1024);
         }
       }
+    };
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the ring is idle
+    zissue(0, 0);
+    for (int c0 = 0, buf = 0; c0 < KC; c0 += ZC, buf ^= 1) {
+      wait_vm_lgkm_barrier<0>();        // batch c0 visible; every wave is done with buffer buf^1
+      if (c0 + ZC < KC) zissue(buf ^ 1, c0 + ZC);
+      const uint8_t* zb0 = smem + buf * kZBuf + lane * 16;
 #pragma unroll
-      for (int j = 0; j < CB; ++j) {
+      for (int j = 0; j < ZC; ++j) {
         if (c0 + j >= KC) break;
+        u32x4 zb[NF];
 #pragma unroll
-        for (int mf = 0; mf < MF; ++mf)
+        for (int nf = 0; nf < NF; ++nf)
+          zb[nf] = *reinterpret_cast<const u32x4*>(zb0 + ((TM / 16 + wn * NF + nf) * ZC + j) * 1024);
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) {
+          const u32x4 za = *reinterpret_cast<const u32x4*>(zb0 + ((wm * MF + mf) * ZC + j) * 1024);
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf)
-            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[j][mf]),
-                                                                   __builtin_bit_cast(bf16x8, zb[j][nf]), acc[mf][nf], 0, 0, 0);
+            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za),
+                                                                   __builtin_bit_cast(bf16x8, zb[nf]), acc[mf][nf], 0, 0, 0);
+        }
       }
     }
   }
