@@ -188,14 +188,18 @@ size_t asgt_bytes(int M, int G, int P) {
 // every outstanding request before each LDS read. Completion is tracked explicitly with
 // s_waitcnt vmcnt before the workgroup barrier (vmcnt completes in order, so the compiler's
 // own waits on its loads stay correct).
+// The compiler's hazard checks do not look inside inline asm, so each helper carries the wait
+// states its operands may need: a vector memory instruction that reads an SGPR written by a VALU
+// instruction (the compiler reloads spilled SGPRs with v_readlane) needs 5, and one that reads M0
+// right after an SALU write of M0 needs 1.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ void lds_dma16_on(const void* g, uint32_t lds, bool on) {
@@ -206,10 +210,10 @@ __device__ __forceinline__ void lds_dma4_on(const void* g, uint32_t lds, bool on
 }
 // scalar base + per-lane 32-bit offset: the per-group address arithmetic stays on the SALU
 __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void lds_dma4_s(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
