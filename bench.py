@@ -65,6 +65,8 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config measurements (merged QKV M=4 P=3, M=8192 gate_up and down)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 64 MiB device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -226,11 +228,95 @@ def main():
                              "timing": f"HIP graph of {C} launches over {C} weight copies, per-launch average"}
         out["decode"] = dec
 
+    # ---- every other configuration: prologue and GEMM timed separately
+    if not args.no_configs:
+        out["configs"] = {"c3_gate_up_m2048": {
+            "prologue_us": out["prologue_us"], "prologue_GBs": out["prologue_gbs"],
+            "gemm_us": out["gemm_us"], "gemm_TFLOPs": out["gemm_tflops"],
+            "gemm_GBs": round(gemm_bytes(M, K, N) / (gemm_ms * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "mfma", "frac": out["roofline"]["frac"]},
+            "timing": "HIP events around each call, eager, DRAM-fed"}}
+        for name, key in (("c2_qkv_m4_p3", "qkv"), ("c4_gate_up_m8192", "full_gate_up"),
+                          ("c4_down_m8192", "full_down")):
+            out["configs"][name] = config_measurement(synth.WORKLOADS[key], pq, torch, np, dev, C)
+
     # ---- the oracle on the host, bounded sample of the same workload
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x0, pl, tl, cl, w, wl)
 
     print(json.dumps(out), flush=True)
+
+
+def config_measurement(wl, pq, torch, np, dev, copies):
+    """Prologue and GEMM of one workload timed separately: per-launch averages of HIP graphs that
+    cycle through weight and activation copies when the call is short (M <= 16), else HIP events
+    around eager calls alternating two copies (one such call streams far more than the 256 MB
+    last-level cache)."""
+    import synth
+    M, K, N, G, P = wl.M, wl.K, wl.N, wl.G, wl.P
+    short = M <= 16
+    C = copies if short else 2
+    x0 = synth.activations(wl)
+    pl, tl, cl = synth.rotations(wl)
+    w = synth.weights(wl)
+    rec = torch.from_numpy(np.stack([pq.build_records(p, t) for p, t in zip(pl, tl)])).to(dev)
+    cs = torch.from_numpy(np.stack(cl)).to(dev)
+    xs = [torch.from_numpy(x0).to(dev) for _ in range(C)]
+    wq0 = pq.pack_weights(torch.from_numpy(w.qweight).to(dev), torch.from_numpy(w.qzeros).to(dev),
+                          torch.from_numpy(w.scales).to(dev))
+    wq = [wq0] + [(wq0[0].clone(), wq0[1].clone()) for _ in range(C - 1)]
+    A = torch.empty((P, M, K), dtype=torch.uint8, device=dev)
+    S = torch.empty((P, M, G), dtype=torch.float32, device=dev)
+    R = torch.empty((P, M, G), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, pq.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
+    pro = lambda i: pq.rotate_quant(xs[i % C], rec, cs, out=(A, S, R))
+    gem = lambda i: pq.gemm(A, S, R, wq[i % C][0], wq[i % C][1], N, *wl.bounds, out=y, workspace=ws)
+
+    def timed(fn, reps):
+        for i in range(C):
+            fn(i)
+        torch.cuda.synchronize()
+        if short:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(C):
+                    fn(i)
+            graph.replay()
+            torch.cuda.synchronize()
+            e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in e:
+                a.record()
+                graph.replay()
+                b.record()
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) for a, b in e])) * 1e-3 / C
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (a, b) in enumerate(e):
+            a.record()
+            fn(i)
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in e])) * 1e-3
+
+    t_pro = timed(pro, 5 if short else 6)
+    t_gem = timed(gem, 5 if short else 6)
+    flops = 2.0 * M * N * K
+    gb = gemm_bytes(M, K, N, P)
+    res = {"M": M, "K": K, "N": N, "partitions": P,
+           "prologue_us": round(t_pro * 1e6, 2),
+           "prologue_GBs": round(prologue_bytes(M, K, P) / t_pro / 1e9, 1),
+           "gemm_us": round(t_gem * 1e6, 2), "gemm_TFLOPs": round(flops / t_gem / 1e12, 2),
+           "gemm_bytes": gb, "gemm_GBs": round(gb / t_gem / 1e9, 1)}
+    if short:
+        res["roofline"] = {"bound": "hbm", "frac": round(gb / t_gem / 1e9 / PEAK_HBM_GBS, 4)}
+        res["timing"] = f"HIP graph of {C} launches over {C} copies, per-launch median of 5 replays"
+    else:
+        res["roofline"] = {"bound": "mfma", "frac": round(flops / t_gem / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        res["timing"] = "HIP events around each eager call, median of 6, two alternating copies"
+    del xs, wq, A, S, R, y, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(x0, pl, tl, cl, w, wl):
