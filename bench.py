@@ -239,10 +239,22 @@ def main():
         for name, key in (("c2_qkv_m4_p3", "qkv"), ("c4_gate_up_m8192", "full_gate_up"),
                           ("c4_down_m8192", "full_down")):
             out["configs"][name] = config_measurement(synth.WORKLOADS[key], pq, torch, np, dev, C)
+        if not args.no_cpu_baseline:
+            for name, key in (("c2_qkv_m4_p3", "qkv"), ("c4_gate_up_m8192", "full_gate_up"),
+                              ("c4_down_m8192", "full_down")):
+                cfg = out["configs"][name]
+                orc = oracle_config_time(synth.WORKLOADS[key], rows=min(synth.WORKLOADS[key].M, 384))
+                gpu_s = (cfg["prologue_us"] + cfg["gemm_us"]) * 1e-6
+                orc["gpu_over_oracle"] = round(orc["full_s_estimate"] / gpu_s, 1)
+                cfg["oracle"] = orc
 
     # ---- the oracle on the host, bounded sample of the same workload
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(x0, pl, tl, cl, w, wl)
+        out["cpu_baseline"], wall = cpu_baseline(x0, pl, tl, cl, w, wl)
+        if "configs" in out:
+            c3 = out["configs"]["c3_gate_up_m2048"]
+            c3["oracle"] = {"rows": wl.M, "full_s": round(wall, 2),
+                            "gpu_over_oracle": round(wall / ((c3["prologue_us"] + c3["gemm_us"]) * 1e-6), 1)}
 
     print(json.dumps(out), flush=True)
 
@@ -319,6 +331,27 @@ def config_measurement(wl, pq, torch, np, dev, copies):
     return res
 
 
+def oracle_config_time(wl, rows):
+    """Wall seconds of the oracle (prologue float32 emulation, then the fp64 GEMM) on the first
+    `rows` token rows of a workload, and that time scaled to all M rows (both parts are linear in
+    the rows)."""
+    import numpy as np
+    import synth
+    from oracle import gemm as ogemm
+    from oracle import prologue as opro
+    x = synth.activations(wl)[:rows]
+    pl, tl, cl = synth.rotations(wl)
+    w = synth.weights(wl)
+    t0 = time.perf_counter()
+    A, S, _ = opro.rotate_quant(x, pl, tl, cl)
+    t1 = time.perf_counter()
+    ogemm.gemm_ref(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds)
+    t2 = time.perf_counter()
+    scale = wl.M / rows
+    return {"rows": rows, "prologue_s": round(t1 - t0, 3), "gemm_s": round(t2 - t1, 3),
+            "full_s_estimate": round((t2 - t0) * scale, 2)}
+
+
 def cpu_baseline(x0, pl, tl, cl, w, wl):
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -336,7 +369,7 @@ def cpu_baseline(x0, pl, tl, cl, w, wl):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{len(rows)} of {wl.M} token rows, all {wl.N} columns, prologue + GEMM "
-                      f"({dt:.1f} s wall; BLAS threads for the per-group fp64 products)"}
+                      f"({dt:.1f} s wall; BLAS threads for the per-group fp64 products)"}, dt
 
 
 if __name__ == "__main__":

@@ -111,6 +111,33 @@ def traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, kernels, source, c
     return rec
 
 
+def counters_table(db, kernels, cus=256, xcds=8, title="", command=""):
+    """Markdown: per-dispatch median of every counter in `db` for each kernel pattern."""
+    cols, rows = _rows(db, "counters_collection")
+    ci = {c: i for i, c in enumerate(cols)}
+    names = sorted({r[ci["counter_name"]] for r in rows})
+    vals = {n: counter_values(db, n) for n in names}
+    lines = []
+    if title:
+        lines.append(f"# {title}\n")
+    if command:
+        lines.append(f"Command: `{command}`\n")
+    lines.append("| kernel | dispatches | " + " | ".join(names) + " | matrix-core busy |")
+    lines.append("|---|---:|" + "---:|" * len(names) + "---:|")
+    for pat in kernels:
+        med = {}
+        n = 0
+        for c in names:
+            v = _match(vals[c], pat)
+            n = len(v)
+            med[c] = statistics.median(v)
+        busy = ""
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("GRBM_GUI_ACTIVE"):
+            busy = f"{med['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * cus * med['GRBM_GUI_ACTIVE'] / xcds):.3f}"
+        lines.append(f"| `{pat}` | {n} | " + " | ".join(f"{med[c]:.4g}" for c in names) + f" | {busy} |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -124,9 +151,18 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, default=64 << 20)
     t.add_argument("--algorithmic-bytes", type=int)
     t.add_argument("--command", action="append", default=[])
+    c = sub.add_parser("counters")
+    c.add_argument("db")
+    c.add_argument("--kernels", required=True)
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--title", default="")
+    c.add_argument("--command", default="")
     a = ap.parse_args(argv)
     if a.cmd == "summary":
         sys.stdout.write(summary(a.db, a.title, a.command))
+    elif a.cmd == "counters":
+        sys.stdout.write(counters_table(a.db, a.kernels.split(","), a.cus, a.xcds, a.title, a.command))
     else:
         rec = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.kernels.split(","), a.source,
                       a.copy_bytes, a.algorithmic_bytes, a.command)
