@@ -74,6 +74,29 @@ const char* pq_last_error(void);
 int pq_build_records(const int16_t* pairs_h, const uint16_t* theta_h, int K, void* rec_h);
 
 /*
+ * Partition plan (host only, load time). A merged linear stacks J projections along N (in this
+ * order), each with its own rotation (pairs, theta, channel scales). Adjacent projections whose
+ * rotation data are bytewise identical merge into one partition, so the GEMM's limit of 3 applies
+ * to runs of distinct rotations, as the loader on the pages does for qwen3_5's in_proj_qkvz (q, k
+ * and v share one rotation: 4 projections, 2 partitions).
+ * Source: "Design" item 4 (partition select, adjacent identical rotations merged into runs) and
+ * "Traps hit" (the 3-partition limit is on distinct rotations).
+ *
+ * J        number of projections, 1..64.
+ * ncols_h  int [J]: columns of each projection, positive multiples of 16.
+ * pairs_h, theta_h, cs_h   J pointers each: int16 [8, K], f16 [8, K/2], f16 [K] (host).
+ * P_out    out: number of partitions (1..3).
+ * pb_out   out int [2]: pb1, pb2 for pq_gemm (PQ_NO_BOUNDARY when unused).
+ * rep_out  out int [3]: for each partition, the first projection of its run (-1 when unused);
+ *          its rotation data go into pq_build_records / the prologue's cs for that partition.
+ * Errors: PQ_ERR_NULL, PQ_ERR_SHAPE, PQ_ERR_PARTITION (more than 3 runs, or a run boundary that
+ *         is not a multiple of 128 columns). Outputs are untouched on error.
+ */
+int pq_plan_partitions(int J, const int* ncols_h, const int16_t* const* pairs_h,
+                       const uint16_t* const* theta_h, const uint16_t* const* cs_h, int K,
+                       int* P_out, int* pb_out, int* rep_out);
+
+/*
  * Weight packing (device, load time): AWQ tensors -> the GEMM's operands.
  *
  * qweight_d int32 [K, N/8], qzeros_d int32 [K/128, N/8]: AWQ words, nibble i of word j holds

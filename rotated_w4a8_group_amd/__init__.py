@@ -40,6 +40,7 @@ SIGNATURES = {
     "pq_abi_version": (_I, []),
     "pq_last_error": (ctypes.c_char_p, []),
     "pq_build_records": (_I, [_P, _P, _I, _P]),
+    "pq_plan_partitions": (_I, [_I, _P, _P, _P, _P, _I, _P, _P, _P]),
     "pq_packed_weight_bytes": (_SZ, [_I, _I]),
     "pq_pack_weights": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
     "pq_rotate_quant": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
@@ -105,6 +106,28 @@ def build_records(pairs, theta):
     _check("pq_build_records", lib().pq_build_records(
         pairs.ctypes.data_as(_P), theta.view(np.uint16).ctypes.data_as(_P), K, out.ctypes.data_as(_P)))
     return out
+
+
+def plan_partitions(projections):
+    """projections: list of (ncols, pairs int16 [8, K], theta f16 [8, K/2], cs f16 [K]) in column
+    order (numpy, host). Adjacent projections with identical rotation data merge into one
+    partition. Returns (P, pb1, pb2, reps): reps[q] is the projection whose rotation partition q
+    uses."""
+    J = len(projections)
+    arrs = [(np.ascontiguousarray(p, dtype=np.int16), np.ascontiguousarray(t, dtype=np.float16).view(np.uint16),
+             np.ascontiguousarray(c, dtype=np.float16).view(np.uint16)) for _, p, t, c in projections]
+    K = arrs[0][0].shape[1] if J else 0
+    for p, t, c in arrs:
+        if p.shape != (LAYERS, K) or t.shape != (LAYERS, K // 2) or c.shape != (K,):
+            raise ValueError("plan_partitions: every projection needs pairs [8, K], theta [8, K/2], cs [K]")
+    ncols = np.array([n for n, *_ in projections], dtype=np.int32)
+    ptrs = [(ctypes.c_void_p * J)(*[a[i].ctypes.data for a in arrs]) for i in range(3)]
+    P = ctypes.c_int()
+    pb = (ctypes.c_int * 2)()
+    rep = (ctypes.c_int * 3)()
+    _check("pq_plan_partitions", lib().pq_plan_partitions(
+        J, ncols.ctypes.data_as(_P), ptrs[0], ptrs[1], ptrs[2], K, ctypes.byref(P), pb, rep))
+    return P.value, pb[0], pb[1], [r for r in rep[:P.value]]
 
 
 def pack_weights(qweight, qzeros, scales, stream=None):

@@ -251,4 +251,48 @@ int pq_build_records(const int16_t* pairs_h, const uint16_t* theta_h, int K, voi
   return PQ_OK;
 }
 
+int pq_plan_partitions(int J, const int* ncols_h, const int16_t* const* pairs_h,
+                       const uint16_t* const* theta_h, const uint16_t* const* cs_h, int K,
+                       int* P_out, int* pb_out, int* rep_out) {
+  using namespace pq;
+  clear_error();
+  if (!ncols_h || !pairs_h || !theta_h || !cs_h || !P_out || !pb_out || !rep_out)
+    return set_error(PQ_ERR_NULL, "pq_plan_partitions: NULL pointer");
+  if (J < 1 || J > 64) return set_error(PQ_ERR_SHAPE, "pq_plan_partitions: J=%d must be in 1..64", J);
+  if (K <= 0 || K % PQ_GROUP) return set_error(PQ_ERR_SHAPE, "pq_plan_partitions: K=%d must be a positive multiple of 128", K);
+  for (int j = 0; j < J; ++j) {
+    if (ncols_h[j] <= 0 || ncols_h[j] % 16)
+      return set_error(PQ_ERR_SHAPE, "pq_plan_partitions: projection %d has %d columns (positive multiple of 16)", j, ncols_h[j]);
+    if (!pairs_h[j] || !theta_h[j] || !cs_h[j]) return set_error(PQ_ERR_NULL, "pq_plan_partitions: NULL rotation data for projection %d", j);
+  }
+  const size_t pb = sizeof(int16_t) * PQ_LAYERS * K, tb = sizeof(uint16_t) * PQ_LAYERS * (K / 2),
+               cb = sizeof(uint16_t) * K;
+  auto same = [&](int a, int b) {
+    return std::memcmp(pairs_h[a], pairs_h[b], pb) == 0 && std::memcmp(theta_h[a], theta_h[b], tb) == 0 &&
+           std::memcmp(cs_h[a], cs_h[b], cb) == 0;
+  };
+  // runs of adjacent projections with identical rotation data
+  int P = 0, rep[PQ_MAX_PARTITIONS], bound[PQ_MAX_PARTITIONS];
+  int64_t col = 0;
+  for (int j = 0; j < J; ++j) {
+    if (j == 0 || !same(j - 1, j)) {
+      if (P == PQ_MAX_PARTITIONS)
+        return set_error(PQ_ERR_PARTITION, "pq_plan_partitions: more than %d runs of distinct rotations", PQ_MAX_PARTITIONS);
+      if (P > 0 && col % PQ_GROUP)
+        return set_error(PQ_ERR_PARTITION, "pq_plan_partitions: a partition boundary at column %lld is not a multiple of 128",
+                         static_cast<long long>(col));
+      rep[P] = j;
+      bound[P] = static_cast<int>(col);
+      ++P;
+    }
+    col += ncols_h[j];
+    if (col > (1 << 24)) return set_error(PQ_ERR_SHAPE, "pq_plan_partitions: too many columns");
+  }
+  *P_out = P;
+  pb_out[0] = P > 1 ? bound[1] : PQ_NO_BOUNDARY;
+  pb_out[1] = P > 2 ? bound[2] : PQ_NO_BOUNDARY;
+  for (int q = 0; q < PQ_MAX_PARTITIONS; ++q) rep_out[q] = q < P ? rep[q] : -1;
+  return PQ_OK;
+}
+
 }  // extern "C"

@@ -219,3 +219,43 @@ def test_hooks_validation():
     assert L.pq_e4m3_encode(FAKE, FAKE, -1, None) == -2
     assert L.pq_e4m3_encode(None, None, 0, None) == 0
     assert L.pq_recip_f32(None, FAKE, 5, None) == -1
+
+
+def _proj(seed, K=256, ncols=128):
+    rng = np.random.default_rng(seed)
+    pairs = np.concatenate([rng.permutation(128) for _ in range(8 * K // 128)]).reshape(8, K).astype(np.int16)
+    theta = rng.uniform(-np.pi, np.pi, (8, K // 2)).astype(np.float16)
+    cs = np.exp(rng.normal(0, 0.3, K)).astype(np.float16)
+    return [ncols, pairs, theta, cs]
+
+
+def test_plan_partitions_pages_examples():
+    """The pages' two examples ("Design" item 4): an attention QKV with three distinct rotations
+    stays at P = 3; in_proj_qkvz, whose q, k and v share one rotation and z has its own, loads as
+    4 projections and plans to P = 2 with the boundary after v."""
+    q, k, v = _proj(1, ncols=256), _proj(2, ncols=128), _proj(3, ncols=128)
+    assert pq.plan_partitions([q, k, v]) == (3, 256, 384, [0, 1, 2])
+    shared = _proj(4, ncols=128)
+    z = _proj(5, ncols=256)
+    qkv_same = [[n] + shared[1:] for n in (256, 128, 128)]
+    assert pq.plan_partitions(qkv_same + [z]) == (2, 512, pq.NO_BOUNDARY, [0, 3])
+    assert pq.plan_partitions([shared]) == (1, pq.NO_BOUNDARY, pq.NO_BOUNDARY, [0])
+
+
+def test_plan_partitions_merges_only_adjacent_and_exact():
+    a, b = _proj(6), _proj(7)
+    # A B A: three runs (identical but not adjacent rotations are not merged)
+    assert pq.plan_partitions([a, b, a])[0] == 3
+    # one f16 ulp in one channel scale breaks the identity
+    a2 = [a[0], a[1], a[2], a[3].copy()]
+    a2[3].view(np.uint16)[17] += 1
+    assert pq.plan_partitions([a, a2])[0] == 2
+    with pytest.raises(pq.PQError) as e:       # four runs
+        pq.plan_partitions([a, b, a, b])
+    assert e.value.code == -4
+    with pytest.raises(pq.PQError) as e:       # a run boundary off the 128-column grid
+        pq.plan_partitions([[144] + a[1:], b])
+    assert e.value.code == -4
+    with pytest.raises(pq.PQError) as e:       # columns not a multiple of 16
+        pq.plan_partitions([[100] + a[1:]])
+    assert e.value.code == -2
