@@ -160,6 +160,31 @@ int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, in
             int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream);
 
 /*
+ * Per-token activation-scale path (device): the same rotation, one e4m3 scale per
+ * (partition, token) instead of per (token, group) -
+ *   amax = max over the whole row of |v|; as = amax * fl32(1/448); codes = e4m3(v * fl32(1/as))
+ *   (same encoder as pq_rotate_quant); rs[g] = fl32(exact sum of the decoded codes of group g).
+ *   An all-zero row gives codes 0, as 0, rs 0.
+ * Source: "Numbers" (the per-token prefill: token scale = the largest group scale, plain
+ * row-sums, the scale applied in the GEMM epilogue), "2026-09-08: MXFP4-PARO prod decode" item 1
+ * (fused prologue, row kept on chip), "2026-09-09 (late)" (plain row-sums, no bf16 scratch row).
+ *
+ * pq_rotate_quant_tok: arguments as pq_rotate_quant, but as_d out f32 [P, M] token scales and
+ *   K <= 18432 (the rotated row is kept on chip: 16 waves x 9 groups).
+ * pq_gemm_tok: arguments as pq_gemm with as_d = AS [P, M] in place of ASG:
+ *   y[m, n] = bf16_rne( as_p[m] * sum_g ( sc[g,n] * sum_{k in g} D(A_p[m,k]) * (c[k,n] - 8)
+ *                                         - fl16(sc[g,n]*(zp[g,n]-8)) * rs_p[m,g] ) )
+ *   The workspace (pq_gemm_tok_workspace_bytes) is needed at every M > 0; no initialisation.
+ */
+int pq_rotate_quant_tok(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const void* rec_d,
+                        const uint16_t* cs_d, uint8_t* a_d, float* as_d, float* rs_d,
+                        pq_stream_t stream);
+size_t pq_gemm_tok_workspace_bytes(int M, int N, int K);
+int pq_gemm_tok(const uint8_t* a_d, const float* as_d, const float* rs_d, int M, int K, int P,
+                const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+                int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream);
+
+/*
  * Verification hooks: run the exact device arithmetic the prologue uses on plain arrays, so
  * tests can check it exhaustively.
  *  pq_e4m3_encode: codes_d[i] = E(q_d[i]) with the prologue's encoder (n >= 0).

@@ -141,6 +141,9 @@ __global__ void pack_zpe_kernel(const uint32_t* __restrict__ sz, int G, int N, u
 // Activation side of the zero-point epilogue, built per GEMM call into the workspace:
 // for partition p, 16-row tile mt and chunk c, 1 KiB where lane l (row 16mt + l%16) holds the
 // 8 bf16 at k' = 32c + 8(l/16) + 0..7 of -[a1 | a1 | a2], ar = asg * rs = a1 + a2 (bf16 pieces).
+// kTok: per-token scales, the operand is the plain row-sum (the row scale comes in the epilogue)
+// and no transposed copy is written.
+template <bool kTok>
 __global__ void zpe_act_kernel(const float* __restrict__ ASG, const float* __restrict__ RS, int M, int G,
                                int P, u32x4* __restrict__ zpa, float* __restrict__ asgt) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -161,14 +164,20 @@ __global__ void zpe_act_kernel(const float* __restrict__ ASG, const float* __res
     if (kp < 3 * G && row < M) {
       const int piece = kp / G, g = kp % G;
       const size_t o = (static_cast<size_t>(p) * M + row) * G + g;
-      const float ar = ASG[o] * RS[o];
-      if (piece == 0) asgt[(static_cast<size_t>(p) * G + g) * M + row] = ASG[o];   // [P][G][M] copy
+      const float ar = kTok ? RS[o] : ASG[o] * RS[o];
+      if (!kTok && piece == 0) asgt[(static_cast<size_t>(p) * G + g) * M + row] = ASG[o];   // [P][G][M] copy
       const uint32_t a1 = f32_to_bf16(ar);
       v = ((piece == 2) ? f32_to_bf16(ar - bf16_to_f32(a1)) : a1) ^ 0x8000u;   // negated
     }
     h[e] = v;
   }
   zpa[idx] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
+
+// Per-token scales broadcast to every group, [P][M][G], for the decode kernel.
+__global__ void tok_expand_kernel(const float* __restrict__ AS, int PM, int G, float* __restrict__ asg) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < static_cast<int64_t>(PM) * G) asg[i] = AS[i / G];
 }
 
 size_t zpe_act_bytes(int M, int G, int P) {
@@ -429,7 +438,7 @@ constexpr int kPfStages = 3;
 constexpr int kPfWaves = 8;
 constexpr int kPfLds = kPfStages * 51200;   // the 256x256 ring (the largest)
 
-template <int TM, int TN, int WM, int WN>
+template <int TM, int TN, int WM, int WN, bool kTok = false>
 struct PfTile {
   static constexpr int MF = TM / WM / 16, NF = TN / WN / 16;   // fragments per wave
   static constexpr int kOffA = 0;                              // [TM rows][8 chunks][16 B], chunks swizzled
@@ -437,7 +446,7 @@ struct PfTile {
   static constexpr int kOffAsg = kOffB + TN * 64;              // [TM] f32
   static constexpr int kOffSz = kOffAsg + TM * 4;              // [TN] u32
   static constexpr int kStage = (kOffSz + TN * 4 + 255) / 256 * 256;
-  static constexpr int nA = TM / 8, nB = TN / 16, nAs = TM / 64, nSz = TN / 64;
+  static constexpr int nA = TM / 8, nB = TN / 16, nAs = kTok ? 0 : TM / 64, nSz = TN / 64;
   static constexpr int nD = nA + nB + nAs + nSz;                // direct loads per group
   static constexpr int kPerWave = (nD + 3) / 4;                 // loads per wave of the issuing half
   static constexpr int kOutStride = TN + 8;                    // bf16 per staged output row
@@ -486,13 +495,13 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
   return bid < 8 * q ? (bid % 8) * q + bid / 8 : bid;
 }
 
-template <int TM, int TN, int WM, int WN>
+template <int TM, int TN, int WM, int WN, bool kTok>
 __device__ __forceinline__ void prefill_tile(
     const uint8_t* __restrict__ A, const float* __restrict__ ASGT, int M, int K,
     const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe, const u32x4* __restrict__ zpa,
     const uint32_t* __restrict__ sz, int N, int p, int m0, int n0, uint16_t* __restrict__ y,
     int64_t ldy, bool vec16, uint8_t* smem) {
-  using TL = PfTile<TM, TN, WM, WN>;
+  using TL = PfTile<TM, TN, WM, WN, kTok>;
   constexpr int MF = TL::MF, NF = TL::NF, PW = TL::kPerWave;
   const int G = K >> 7;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -592,19 +601,28 @@ __device__ __forceinline__ void prefill_tile(
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap + aoff0);
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + aoff1);
         const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        asb[mf & 1] = *reinterpret_cast<const float4*>(st + TL::kOffAsg + (wm * MF * 16 + 16 * mf + 4 * kq) * 4);
+        if constexpr (!kTok)
+          asb[mf & 1] = *reinterpret_cast<const float4*>(st + TL::kOffAsg + (wm * MF * 16 + 16 * mf + 4 * kq) * 4);
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf) Tb[mf & 1][nf] = mfma_fp8(a, bf[nf]);
       }
       if (mf > 0) {
         const int pm = mf - 1;
-        const float4 as = asb[pm & 1];
+        if constexpr (kTok) {
+          // per-token scales: the row scale is applied once in the epilogue
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) {
-          acc[pm][nf][0] = __builtin_fmaf(as.x * s9[nf], Tb[pm & 1][nf][0], acc[pm][nf][0]);
-          acc[pm][nf][1] = __builtin_fmaf(as.y * s9[nf], Tb[pm & 1][nf][1], acc[pm][nf][1]);
-          acc[pm][nf][2] = __builtin_fmaf(as.z * s9[nf], Tb[pm & 1][nf][2], acc[pm][nf][2]);
-          acc[pm][nf][3] = __builtin_fmaf(as.w * s9[nf], Tb[pm & 1][nf][3], acc[pm][nf][3]);
+          for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[pm][nf][i] = __builtin_fmaf(s9[nf], Tb[pm & 1][nf][i], acc[pm][nf][i]);
+        } else {
+          const float4 as = asb[pm & 1];
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) {
+            acc[pm][nf][0] = __builtin_fmaf(as.x * s9[nf], Tb[pm & 1][nf][0], acc[pm][nf][0]);
+            acc[pm][nf][1] = __builtin_fmaf(as.y * s9[nf], Tb[pm & 1][nf][1], acc[pm][nf][1]);
+            acc[pm][nf][2] = __builtin_fmaf(as.z * s9[nf], Tb[pm & 1][nf][2], acc[pm][nf][2]);
+            acc[pm][nf][3] = __builtin_fmaf(as.w * s9[nf], Tb[pm & 1][nf][3], acc[pm][nf][3]);
+          }
         }
       }
     }
@@ -661,6 +679,18 @@ __device__ __forceinline__ void prefill_tile(
     }
   }
 
+  if constexpr (kTok) {
+    // per-token scale of each row (ASGT holds AS [P][M] in this mode)
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = min(m0 + wm * MF * 16 + 16 * mf + 4 * kq + i, M - 1);
+        const float a = ASGT[static_cast<size_t>(p) * M + row];
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) acc[mf][nf][i] *= a;
+      }
+  }
   // ---- bf16 tile through LDS (the ring is idle now), then whole rows with wide stores
   __syncthreads();   // every wave has finished reading the ring
   uint16_t* ot = reinterpret_cast<uint16_t*>(smem);
@@ -684,6 +714,7 @@ struct PrefillMap {
   int wide;      // 1: 256x256 tiles, 0: 128x128 tiles
 };
 
+template <bool kTok>
 __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ ASGT, int M, int K,
     const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe, const u32x4* __restrict__ zpa,
@@ -705,13 +736,13 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
   if (m0 >= M || n0 >= N) return;   // a piece wholly past the matrix
   const int p = (n0 >= pb1) + (n0 >= pb2);
   if (map.wide) {
-    if (split == 1) prefill_tile<256, 256, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else if (split == 2) prefill_tile<128, 256, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else if (split == 4) prefill_tile<128, 128, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (split == 1) prefill_tile<256, 256, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 2) prefill_tile<128, 256, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 4) prefill_tile<128, 128, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
   } else {
-    if (split == 1) prefill_tile<128, 128, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (split == 1) prefill_tile<128, 128, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
   }
 }
 
@@ -796,56 +827,113 @@ size_t pq_gemm_workspace_bytes(int M, int N, int K) {
   return pq::zpe_act_bytes(M, K / PQ_GROUP, PQ_MAX_PARTITIONS) + pq::asgt_bytes(M, K / PQ_GROUP, PQ_MAX_PARTITIONS);
 }
 
-int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
-            const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
-            int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream) {
-  using namespace pq;
-  clear_error();
-  if (M < 0) return set_error(PQ_ERR_SHAPE, "pq_gemm: M=%d < 0", M);
-  if (K <= 0 || K % PQ_GROUP || K > (1 << 24)) return set_error(PQ_ERR_SHAPE, "pq_gemm: K=%d must be a positive multiple of 128", K);
-  if (N <= 0 || N % 16 || N > (1 << 24)) return set_error(PQ_ERR_SHAPE, "pq_gemm: N=%d must be a positive multiple of 16", N);
-  if (ldy < N || (ldy & 1)) return set_error(PQ_ERR_SHAPE, "pq_gemm: ldy=%lld must be even and >= N=%d", static_cast<long long>(ldy), N);
-  const int perr = check_partitions(P, pb1, pb2, N);
-  if (perr != PQ_OK) return perr;
-  if (ws_bytes < pq_gemm_workspace_bytes(M, N, K)) return set_error(PQ_ERR_WORKSPACE, "pq_gemm: workspace too small");
-  if (M == 0) return PQ_OK;
-  if (!a_d || !asg_d || !rs_d || !wpk_d || !sz_d || !y_d) return set_error(PQ_ERR_NULL, "pq_gemm: NULL pointer");
-  if (pq_gemm_workspace_bytes(M, N, K) && !ws_d) return set_error(PQ_ERR_NULL, "pq_gemm: NULL workspace");
-  if (!aligned(a_d, 16) || !aligned(asg_d, 4) || !aligned(rs_d, 4) || !aligned(wpk_d, 16) || !aligned(sz_d, 4) ||
-      !aligned(y_d, 4) || !aligned(ws_d, 16))
-    return set_error(PQ_ERR_ALIGN, "pq_gemm: misaligned pointer");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+size_t pq_gemm_tok_workspace_bytes(int M, int N, int K) {
+  (void)N;
+  if (M <= 0 || K <= 0 || K % PQ_GROUP) return 0;
+  const int G = K / PQ_GROUP;
+  if (M <= 16) return (static_cast<size_t>(PQ_MAX_PARTITIONS) * M * G * 4 + 255) / 256 * 256;   // scales per group
+  return pq::zpe_act_bytes(M, G, PQ_MAX_PARTITIONS);
+}
+
+}  // extern "C"
+
+namespace pq {
+
+// The GEMM behind pq_gemm (kTok = false: a_scale = ASG [P, M, G]) and pq_gemm_tok (kTok = true:
+// a_scale = AS [P, M]); validation is the caller's.
+template <bool kTok>
+static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scale, const float* rs_d, int M, int K,
+                       int P, const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+                       int64_t ldy, void* ws_d, hipStream_t s) {
   const int G = K / PQ_GROUP;
   const u32x4* wpk = static_cast<const u32x4*>(wpk_d);
   const uint32_t* sz = reinterpret_cast<const uint32_t*>(sz_d);
   if (M <= 16) {
+    const float* asg = a_scale;
+    if (kTok) {
+      // the decode kernel folds per group: give every group the token's scale
+      float* ex = static_cast<float*>(ws_d);
+      const int64_t n = static_cast<int64_t>(P) * M * G;
+      hipLaunchKernelGGL(tok_expand_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                         a_scale, P * M, G, ex);
+      asg = ex;
+    }
     DecodeMap map;
     decode_map(N, pb1, pb2, cu_count(), &map);
     hipLaunchKernelGGL(gemm_decode_kernel, dim3(map.wg0[3]), dim3(64 * kDecWaves), 0, s,
-                       a_d, asg_d, rs_d, M, K, wpk, sz, N, map, y_d, ldy);
-    return launch_status("pq_gemm(decode)");
+                       a_d, asg, rs_d, M, K, wpk, sz, N, map, y_d, ldy);
+    return launch_status(what);
   }
   // 256x256 tiles (one workgroup per CU) unless a partition boundary is not on a 256-column line
   const bool wide = (pb1 >= N || pb1 % 256 == 0) && (pb2 >= N || pb2 % 256 == 0);
   const int bt = wide ? 256 : 128;
   const int64_t tiles = static_cast<int64_t>((M + bt - 1) / bt) * ((N + bt - 1) / bt);
-  if (tiles * 8 > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "pq_gemm: problem too large");
+  if (tiles * 8 > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "%s: problem too large", what);
   // the prefill kernel addresses a partition's activations with 32-bit lane offsets
   if (static_cast<int64_t>(M) * K > 0x7FFFFFFF || static_cast<int64_t>(M) * (K / PQ_GROUP) * 4 > 0x7FFFFFFF)
-    return set_error(PQ_ERR_SHAPE, "pq_gemm: M * K too large for one call (split the rows)");
+    return set_error(PQ_ERR_SHAPE, "%s: M * K too large for one call (split the rows)", what);
   const PrefillMap map = prefill_map(M, N, wide, cu_count());
   const int64_t grid = static_cast<int64_t>(map.full) + static_cast<int64_t>(map.ntiles - map.full) * map.split;
   const u32x4* zpe = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(wpk_d) + static_cast<size_t>(K) * N / 2);
   u32x4* zpa = static_cast<u32x4*>(ws_d);
-  float* asgt = reinterpret_cast<float*>(static_cast<uint8_t*>(ws_d) + zpe_act_bytes(M, G, PQ_MAX_PARTITIONS));
+  float* asgt = kTok ? nullptr
+                     : reinterpret_cast<float*>(static_cast<uint8_t*>(ws_d) + zpe_act_bytes(M, G, PQ_MAX_PARTITIONS));
   const int64_t zt = static_cast<int64_t>(P) * ((M + 15) / 16) * zpe_chunks(G) * 64;
-  hipLaunchKernelGGL(zpe_act_kernel, dim3(static_cast<unsigned>((zt + 255) / 256)), dim3(256), 0, s,
-                     asg_d, rs_d, M, G, P, zpa, asgt);
+  hipLaunchKernelGGL(zpe_act_kernel<kTok>, dim3(static_cast<unsigned>((zt + 255) / 256)), dim3(256), 0, s,
+                     a_scale, rs_d, M, G, P, zpa, asgt);
   // 16-byte output stores need a 16-byte aligned y and a row pitch of 8 elements
   const bool vec16 = aligned(y_d, 16) && ldy % 8 == 0;
-  hipLaunchKernelGGL(gemm_prefill_kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * kPfWaves), 0, s,
-                     a_d, asgt, M, K, wpk, zpe, zpa, sz, N, pb1, pb2, y_d, ldy, map, vec16);
-  return launch_status("pq_gemm(prefill)");
+  hipLaunchKernelGGL(gemm_prefill_kernel<kTok>, dim3(static_cast<unsigned>(grid)), dim3(64 * kPfWaves), 0, s,
+                     a_d, kTok ? a_scale : asgt, M, K, wpk, zpe, zpa, sz, N, pb1, pb2, y_d, ldy, map, vec16);
+  return launch_status(what);
+}
+
+// Shared validation of pq_gemm / pq_gemm_tok; returns PQ_OK to go on, 1 for the M == 0 no-op.
+static int gemm_check(const char* what, const uint8_t* a_d, const float* scale_d, const float* rs_d, int M, int K,
+                      int P, const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+                      int64_t ldy, void* ws_d, size_t ws_bytes, size_t ws_need) {
+  if (M < 0) return set_error(PQ_ERR_SHAPE, "%s: M=%d < 0", what, M);
+  if (K <= 0 || K % PQ_GROUP || K > (1 << 24)) return set_error(PQ_ERR_SHAPE, "%s: K=%d must be a positive multiple of 128", what, K);
+  if (N <= 0 || N % 16 || N > (1 << 24)) return set_error(PQ_ERR_SHAPE, "%s: N=%d must be a positive multiple of 16", what, N);
+  if (ldy < N || (ldy & 1)) return set_error(PQ_ERR_SHAPE, "%s: ldy=%lld must be even and >= N=%d", what, static_cast<long long>(ldy), N);
+  const int perr = check_partitions(P, pb1, pb2, N);
+  if (perr != PQ_OK) return perr;
+  if (ws_bytes < ws_need) return set_error(PQ_ERR_WORKSPACE, "%s: workspace too small", what);
+  if (M == 0) return 1;
+  if (!a_d || !scale_d || !rs_d || !wpk_d || !sz_d || !y_d) return set_error(PQ_ERR_NULL, "%s: NULL pointer", what);
+  if (ws_need && !ws_d) return set_error(PQ_ERR_NULL, "%s: NULL workspace", what);
+  if (!aligned(a_d, 16) || !aligned(scale_d, 4) || !aligned(rs_d, 4) || !aligned(wpk_d, 16) || !aligned(sz_d, 4) ||
+      !aligned(y_d, 4) || !aligned(ws_d, 16))
+    return set_error(PQ_ERR_ALIGN, "%s: misaligned pointer", what);
+  return PQ_OK;
+}
+
+}  // namespace pq
+
+extern "C" {
+
+int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
+            const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+            int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream) {
+  using namespace pq;
+  clear_error();
+  const int rc = gemm_check("pq_gemm", a_d, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d, ws_bytes,
+                            pq_gemm_workspace_bytes(M, N, K));
+  if (rc != PQ_OK) return rc == 1 ? PQ_OK : rc;
+  return gemm_launch<false>("pq_gemm", a_d, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
+                            reinterpret_cast<hipStream_t>(stream));
+}
+
+int pq_gemm_tok(const uint8_t* a_d, const float* as_d, const float* rs_d, int M, int K, int P,
+                const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+                int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream) {
+  using namespace pq;
+  clear_error();
+  const int rc = gemm_check("pq_gemm_tok", a_d, as_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
+                            ws_bytes, pq_gemm_tok_workspace_bytes(M, N, K));
+  if (rc != PQ_OK) return rc == 1 ? PQ_OK : rc;
+  return gemm_launch<true>("pq_gemm_tok", a_d, as_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
+                           reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

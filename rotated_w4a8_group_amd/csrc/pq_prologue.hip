@@ -245,6 +245,120 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Per-token variant: one e4m3 scale per (partition, token) = the largest of the token's group
+// scales ("Numbers", the per-token prefill bullet; section "2026-09-08: MXFP4-PARO prod decode",
+// item 1). The scale needs every group of the row before any code is written, so a 16-wave
+// workgroup takes one quad of 4 tokens across all G groups: wave w rotates groups w, w+16, ...
+// through its own LDS quad image (the per-group kernel's layout and record lane order) and keeps
+// the rotated values in registers (8 per lane per group, at most NPG groups); a workgroup-wide
+// max gives the token amax, then every wave encodes its parked groups and writes plain per-group
+// code row-sums.
+constexpr int kTokWaves = 16;
+
+template <int NPG, bool kVec16>
+__global__ __launch_bounds__(64 * kTokWaves) void rotate_quant_tok_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int M, int K, int P,
+    const uint2* __restrict__ rec, const uint16_t* __restrict__ cs, uint8_t* __restrict__ A,
+    float* __restrict__ AS, float* __restrict__ RS) {
+  __shared__ __align__(16) uint8_t qbuf[kTokWaves][kProQuadBytes];
+  __shared__ float tred[kTokWaves][4];
+
+  const int G = K >> 7, half = K >> 1;
+  const int quads = (M + 3) >> 2;
+  const int p = blockIdx.x / quads, m0 = 4 * (blockIdx.x % quads);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, t = lane >> 4, c = lane & 15;
+  const int m = m0 + t, mld = min(m, M - 1);      // clamped: always a valid row to read
+  uint8_t* const buf = qbuf[wave];
+  uint8_t* const slot = buf + (9 * c) * 16 + 4 * t;
+  const uint16_t* const xrow = x + static_cast<size_t>(mld) * ldx + 8 * c;
+  const uint16_t* const csp = cs + static_cast<size_t>(p) * K + 8 * c;
+  const uint2* const recp = rec + static_cast<size_t>(p) * PQ_LAYERS * half + lane;
+
+  float park[NPG][8];
+  float tmax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NPG; ++j) {
+    const int g = wave + kTokWaves * j;
+    if (g < G) {
+      uint2 q[PQ_LAYERS];
+#pragma unroll
+      for (int r = 0; r < PQ_LAYERS; ++r) q[r] = recp[static_cast<size_t>(r) * half + g * 64];
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(csp + g * 128);
+      const uint32_t cs4[4] = {cw[0], cw[1], cw[2], cw[3]};
+      const uint4 xs = load_x8<kVec16>(xrow + g * 128);
+      const uint32_t xw[4] = {xs.x, xs.y, xs.z, xs.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<float*>(slot + (2 * i) * 16) = half_lo(xw[i]) * half_lo(cs4[i]);
+        *reinterpret_cast<float*>(slot + (2 * i + 1) * 16) = half_hi(xw[i]) * half_hi(cs4[i]);
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < PQ_LAYERS; ++r) {
+        const uint32_t ta = lds_row_bytes(q[r].x & 0x7Fu), ha = lds_row_bytes((q[r].x >> 8) & 0x7Fu);
+        const float cr = f16_to_f32(q[r].y), sr = f16_to_f32(q[r].y >> 16);
+        const float4 a = *reinterpret_cast<const float4*>(buf + ta);
+        const float4 b = *reinterpret_cast<const float4*>(buf + ha);
+        const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+        float na[4], nb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float ca = cr * av[k], sb = sr * bv[k];
+          const float cb = cr * bv[k], sa = sr * av[k];
+          na[k] = ca + sb;
+          nb[k] = cb - sa;
+        }
+        *reinterpret_cast<float4*>(buf + ta) = make_float4(na[0], na[1], na[2], na[3]);
+        *reinterpret_cast<float4*>(buf + ha) = make_float4(nb[0], nb[1], nb[2], nb[3]);
+        __builtin_amdgcn_wave_barrier();
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        park[j][i] = *reinterpret_cast<const float*>(slot + i * 16);
+        tmax = __builtin_fmaxf(tmax, __builtin_fabsf(park[j][i]));
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+
+  // token amax: over the 16 lanes of the token, then over the waves
+  tmax = row_max(tmax);
+  if (c == 0) tred[wave][t] = tmax;
+  __syncthreads();
+  float amax = tred[0][t];
+#pragma unroll
+  for (int w = 1; w < kTokWaves; ++w) amax = __builtin_fmaxf(amax, tred[w][t]);
+  const float as = amax * 0x1.24924ap-9f;   // fl32(1/448)
+  const float inv = recip_rn(as);
+  const bool inv_bad = __builtin_fabsf(inv) == __builtin_inff();
+  const size_t row = static_cast<size_t>(p) * M + m;
+  if (wave == 0 && c == 0 && m < M) AS[row] = as;
+
+#pragma unroll
+  for (int j = 0; j < NPG; ++j) {
+    const int g = wave + kTokWaves * j;
+    if (g < G) {
+      float s[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = park[j][i] * inv + 0.0f;
+      uint32_t w0 = pack4(s[0], s[1], s[2], s[3]), w1 = pack4(s[4], s[5], s[6], s[7]);
+      const uint32_t bad = (nan_bytes(w0) | nan_bytes(w1)) | (inv_bad ? 1u : 0u);
+      if (__builtin_amdgcn_ballot_w64(bad != 0)) {
+        // rare: a NaN or out-of-range value in the wave; the full encoder
+        w0 = e4m3_encode2(park[j][0] * inv, park[j][1] * inv) | (e4m3_encode2(park[j][2] * inv, park[j][3] * inv) << 16);
+        w1 = e4m3_encode2(park[j][4] * inv, park[j][5] * inv) | (e4m3_encode2(park[j][6] * inv, park[j][7] * inv) << 16);
+      }
+      const int units = row_sum(code_units(w0, w1));
+      if (m < M) {
+        *reinterpret_cast<uint2*>(A + row * K + g * 128 + 8 * c) = make_uint2(w0, w1);
+        if (c == 0) RS[row * G + g] = static_cast<float>(units) * 0x1p-9f;
+      }
+    }
+  }
+}
+
 __global__ void e4m3_encode_kernel(const float* __restrict__ q, uint8_t* __restrict__ out, int64_t n) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 2;
   if (i + 1 < n) {
@@ -300,6 +414,42 @@ int pq_rotate_quant(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const
                      static_cast<const uint2*>(rec_d), cs_d, a_d, asg_d, rs_d, tok,
                      static_cast<int>(chunks));
   return launch_status("pq_rotate_quant");
+}
+
+int pq_rotate_quant_tok(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const void* rec_d,
+                        const uint16_t* cs_d, uint8_t* a_d, float* as_d, float* rs_d,
+                        pq_stream_t stream) {
+  using namespace pq;
+  clear_error();
+  if (M < 0) return set_error(PQ_ERR_SHAPE, "pq_rotate_quant_tok: M=%d < 0", M);
+  if (K <= 0 || K % PQ_GROUP || K > kTokWaves * 9 * PQ_GROUP)
+    return set_error(PQ_ERR_SHAPE, "pq_rotate_quant_tok: K=%d must be a positive multiple of 128, at most %d", K,
+                     kTokWaves * 9 * PQ_GROUP);
+  if (P < 1 || P > PQ_MAX_PARTITIONS) return set_error(PQ_ERR_PARTITION, "pq_rotate_quant_tok: P=%d must be in 1..3", P);
+  if (ldx < K || (ldx & 1)) return set_error(PQ_ERR_SHAPE, "pq_rotate_quant_tok: ldx=%lld must be even and >= K=%d", static_cast<long long>(ldx), K);
+  if (M == 0) return PQ_OK;
+  if (!x_d || !rec_d || !cs_d || !a_d || !as_d || !rs_d) return set_error(PQ_ERR_NULL, "pq_rotate_quant_tok: NULL pointer");
+  if (!aligned(x_d, 4) || !aligned(rec_d, 8) || !aligned(cs_d, 4) || !aligned(a_d, 16) || !aligned(as_d, 4) || !aligned(rs_d, 4))
+    return set_error(PQ_ERR_ALIGN, "pq_rotate_quant_tok: misaligned pointer");
+  const int G = K / PQ_GROUP;
+  const int64_t blocks = static_cast<int64_t>(P) * ((M + 3) / 4);
+  if (blocks > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "pq_rotate_quant_tok: problem too large");
+  const bool vec16 = aligned(x_d, 16) && (ldx % 8) == 0;
+  const int npg = (G + kTokWaves - 1) / kTokWaves;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const uint2* rec = static_cast<const uint2*>(rec_d);
+#define PQ_TOK_LAUNCH(NPG)                                                                          \
+  do {                                                                                              \
+    auto kern = vec16 ? rotate_quant_tok_kernel<NPG, true> : rotate_quant_tok_kernel<NPG, false>;   \
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * kTokWaves), 0, s, x_d, ldx, \
+                       M, K, P, rec, cs_d, a_d, as_d, rs_d);                                        \
+  } while (0)
+  if (npg <= 1) PQ_TOK_LAUNCH(1);
+  else if (npg <= 3) PQ_TOK_LAUNCH(3);
+  else if (npg <= 5) PQ_TOK_LAUNCH(5);
+  else PQ_TOK_LAUNCH(9);
+#undef PQ_TOK_LAUNCH
+  return launch_status("pq_rotate_quant_tok");
 }
 
 int pq_e4m3_encode(const float* q_d, uint8_t* codes_d, int64_t n, pq_stream_t stream) {
