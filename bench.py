@@ -244,6 +244,11 @@ def main():
         for name, key in (("c3_gate_up_m2048", "prefill"), ("c4_gate_up_m8192", "full_gate_up"),
                           ("c4_down_m8192", "full_down")):
             out["per_token"][name] = config_measurement(synth.WORKLOADS[key], pq, torch, np, dev, C, tok=True)
+        # the per-group int8 activation mode
+        out["int8_per_group"] = {}
+        for name, key in (("c1_decode_m1", "decode_m1"), ("c3_gate_up_m2048", "prefill"),
+                          ("c4_down_m8192", "full_down")):
+            out["int8_per_group"][name] = config_measurement(synth.WORKLOADS[key], pq, torch, np, dev, C, i8=True)
         if not args.no_cpu_baseline:
             for name, key in (("c2_qkv_m4_p3", "qkv"), ("c4_gate_up_m8192", "full_gate_up"),
                               ("c4_down_m8192", "full_down")):
@@ -264,7 +269,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def config_measurement(wl, pq, torch, np, dev, copies, tok=False):
+def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False):
     """Prologue and GEMM of one workload timed separately: per-launch averages of HIP graphs that
     cycle through weight and activation copies when the call is short (M <= 16), else HIP events
     around eager calls alternating two copies (one such call streams far more than the 256 MB
@@ -282,7 +287,7 @@ def config_measurement(wl, pq, torch, np, dev, copies, tok=False):
     wq0 = pq.pack_weights(torch.from_numpy(w.qweight).to(dev), torch.from_numpy(w.qzeros).to(dev),
                           torch.from_numpy(w.scales).to(dev))
     wq = [wq0] + [(wq0[0].clone(), wq0[1].clone()) for _ in range(C - 1)]
-    A = torch.empty((P, M, K), dtype=torch.uint8, device=dev)
+    A = torch.empty((P, M, K), dtype=torch.int8 if i8 else torch.uint8, device=dev)
     S = torch.empty((P, M) if tok else (P, M, G), dtype=torch.float32, device=dev)
     R = torch.empty((P, M, G), dtype=torch.float32, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -290,6 +295,10 @@ def config_measurement(wl, pq, torch, np, dev, copies, tok=False):
         ws = torch.empty(max(1, pq.gemm_tok_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
         pro = lambda i: pq.rotate_quant_tok(xs[i % C], rec, cs, out=(A, S, R))
         gem = lambda i: pq.gemm_tok(A, S, R, wq[i % C][0], wq[i % C][1], N, *wl.bounds, out=y, workspace=ws)
+    elif i8:
+        ws = torch.empty(max(1, pq.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
+        pro = lambda i: pq.rotate_quant_i8(xs[i % C], rec, cs, out=(A, S, R))
+        gem = lambda i: pq.gemm_i8(A, S, R, wq[i % C][0], wq[i % C][1], N, *wl.bounds, out=y, workspace=ws)
     else:
         ws = torch.empty(max(1, pq.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
         pro = lambda i: pq.rotate_quant(xs[i % C], rec, cs, out=(A, S, R))

@@ -185,6 +185,26 @@ int pq_gemm_tok(const uint8_t* a_d, const float* as_d, const float* rs_d, int M,
                 int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream);
 
 /*
+ * Per-group int8 activation mode (device): the same rotation and per-(token, group) scales with
+ * int8 codes -
+ *   amax = max over the group of |v|; asg = fl32(amax / 127); codes = clamp(round-half-even(
+ *   fl32(v * fl32(1/asg))), -127, 127); rs = the integer sum of the group's codes (as f32).
+ *   An all-zero group gives codes 0, asg 0, rs 0.
+ * pq_gemm_i8: arguments as pq_gemm with int8 codes; the same formula with D(A) replaced by the
+ *   integer code (products on the integer matrix core, exact in int32 per group).
+ * Source: "2026-09-11: I8 mode -- int8 activations on the iu8 WMMA" (scale amax/127, round and
+ * clamp to +-127, integer row-sums, integer products, the e4m3 path's fold algebra and SZ),
+ * "2026-09-11 (evening): per-group int8 on the A-tiled band" (per-group granularity).
+ * pq_rotate_quant_i8: arguments as pq_rotate_quant; a_d out int8 [P, M, K], 16-byte aligned.
+ */
+int pq_rotate_quant_i8(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const void* rec_d,
+                       const uint16_t* cs_d, int8_t* a_d, float* asg_d, float* rs_d,
+                       pq_stream_t stream);
+int pq_gemm_i8(const int8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
+               const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+               int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream);
+
+/*
  * Verification hooks: run the exact device arithmetic the prologue uses on plain arrays, so
  * tests can check it exhaustively.
  *  pq_e4m3_encode: codes_d[i] = E(q_d[i]) with the prologue's encoder (n >= 0).

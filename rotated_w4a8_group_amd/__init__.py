@@ -49,6 +49,8 @@ SIGNATURES = {
     "pq_rotate_quant_tok": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "pq_gemm_tok_workspace_bytes": (_SZ, [_I, _I, _I]),
     "pq_gemm_tok": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
+    "pq_rotate_quant_i8": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "pq_gemm_i8": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
     "pq_e4m3_encode": (_I, [_P, _P, _I64, _P]),
     "pq_recip_f32": (_I, [_P, _P, _I64, _P]),
 }
@@ -192,6 +194,50 @@ def gemm(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, wor
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
     _check("pq_gemm", lib().pq_gemm(
+        _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2,
+        _ptr(out), out.stride(0), _ptr(workspace), ws_bytes if workspace is not None else 0, _stream(stream)))
+    return out
+
+
+def rotate_quant_i8(x, rec, cs, out=None, stream=None):
+    """Per-group int8 mode: x f16 [M, K], rec [P, 8, K/2, 8], cs f16 [P, K] -> (A int8 [P, M, K],
+    ASG f32 [P, M, G], RS f32 [P, M, G])."""
+    import torch
+    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise TypeError("x: expected a CUDA float16 [M, K] tensor with unit column stride")
+    _need(rec, torch.uint8, "rec")
+    _need(cs, torch.float16, "cs")
+    M, K = x.shape
+    P = cs.shape[0] if cs.dim() == 2 else 1
+    G = K // GROUP
+    if out is None:
+        A = torch.empty((P, M, K), dtype=torch.int8, device=x.device)
+        ASG = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
+        RS = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
+    else:
+        A, ASG, RS = out
+    _check("pq_rotate_quant_i8", lib().pq_rotate_quant_i8(
+        _ptr(x), x.stride(0), M, K, P, _ptr(rec), _ptr(cs), _ptr(A), _ptr(ASG), _ptr(RS), _stream(stream)))
+    return A, ASG, RS
+
+
+def gemm_i8(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, workspace=None, stream=None):
+    """Per-group int8 GEMM: A int8 [P, M, K], ASG/RS f32 [P, M, G], packed weights -> y bf16."""
+    import torch
+    _need(A, torch.int8, "A")
+    _need(ASG, torch.float32, "ASG")
+    _need(RS, torch.float32, "RS")
+    _need(wpk, torch.uint8, "wpk")
+    _need(sz, torch.float16, "sz")
+    P, M, K = A.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
+        raise TypeError("out: expected a bf16 [M, ldy] tensor with unit column stride")
+    ws_bytes = gemm_workspace_bytes(M, N, K)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
+    _check("pq_gemm_i8", lib().pq_gemm_i8(
         _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2,
         _ptr(out), out.stride(0), _ptr(workspace), ws_bytes if workspace is not None else 0, _stream(stream)))
     return out

@@ -37,6 +37,26 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Integer-code product of one 128-group: two 16x16x64 int8 matrix-core steps over the same
+// 32-byte fragments as the fp8 step (each step pairs the same byte positions of A and B, so the
+// two halves together cover every k of the group once); exact in int32, returned as float.
+__device__ __forceinline__ v4f mfma_i8(const v8i& a, const v8i& b) {
+  v4i c = {0, 0, 0, 0};
+  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{a[0], a[1], a[2], a[3]}, v4i{b[0], b[1], b[2], b[3]}, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{a[4], a[5], a[6], a[7]}, v4i{b[4], b[5], b[6], b[7]}, c, 0, 0, 0);
+  return v4f{static_cast<float>(c[0]), static_cast<float>(c[1]), static_cast<float>(c[2]), static_cast<float>(c[3])};
+}
+
+// The group product for either activation code domain: e4m3 codes times the raw weight codes as
+// e4m3 values c * 2^-9, or int8 codes times the raw codes as integers.
+template <bool kI8>
+__device__ __forceinline__ v4f group_product(const v8i& a, const v8i& b) {
+  if constexpr (kI8) return mfma_i8(a, b);
+  else return mfma_fp8(a, b);
+}
+
 __device__ __forceinline__ v8i unpack_codes(const u32x4& w) {
   v8i b;
   b[0] = static_cast<int>(w.x & 0x0F0F0F0Fu);
@@ -267,7 +287,7 @@ struct DecodeSlot {
 };
 
 // MR = activation rows held per lane that can be live (1 when M == 1, else 4)
-template <int NT, int MR>
+template <int NT, int MR, bool kI8>
 __device__ __forceinline__ void decode_body(
     const uint8_t* __restrict__ A, const float* __restrict__ asgp, const float* __restrict__ rsp,
     int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ sz, int N, int p,
@@ -338,8 +358,9 @@ __device__ __forceinline__ void decode_body(
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const u32x4 bw = *reinterpret_cast<const u32x4*>(sp + t * 1024 + 16 * lane);
-      const float2 f = sz_factors(*reinterpret_cast<const uint32_t*>(sp + S::kOffSz + 4 * (16 * t + col)));
-      const v4f T = mfma_fp8(av, unpack_codes(bw));
+      float2 f = sz_factors(*reinterpret_cast<const uint32_t*>(sp + S::kOffSz + 4 * (16 * t + col)));
+      if constexpr (kI8) f.x *= 0x1p-9f;   // integer products carry no 2^-9
+      const v4f T = group_product<kI8>(av, unpack_codes(bw));
 #pragma unroll
       for (int i = 0; i < MR; ++i) acc[t][i] += as[i] * (f.x * T[i] - f.y * rs[i]);
     }
@@ -363,6 +384,7 @@ __device__ __forceinline__ void decode_body(
   }
 }
 
+template <bool kI8>
 __global__ __launch_bounds__(64 * kDecWaves, kDecPerCU) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ ASG, const float* __restrict__ RS,
     int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ sz, int N,
@@ -379,8 +401,8 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecPerCU) void gemm_decode_kernel(
   const float* rsp = RS + q * MG;
 #define PQ_DECODE_CASE(n)                                                                      \
   case n:                                                                                      \
-    if (M == 1) decode_body<n, 1>(A, asgp, rsp, M, K, wpk, sz, N, q, tfirst, y, ldy, smem);   \
-    else decode_body<n, 4>(A, asgp, rsp, M, K, wpk, sz, N, q, tfirst, y, ldy, smem);          \
+    if (M == 1) decode_body<n, 1, kI8>(A, asgp, rsp, M, K, wpk, sz, N, q, tfirst, y, ldy, smem);   \
+    else decode_body<n, 4, kI8>(A, asgp, rsp, M, K, wpk, sz, N, q, tfirst, y, ldy, smem);          \
     break;
   switch (cnt) {
     PQ_DECODE_CASE(1) PQ_DECODE_CASE(2) PQ_DECODE_CASE(3)
@@ -495,7 +517,7 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
   return bid < 8 * q ? (bid % 8) * q + bid / 8 : bid;
 }
 
-template <int TM, int TN, int WM, int WN, bool kTok>
+template <int TM, int TN, int WM, int WN, bool kTok, bool kI8>
 __device__ __forceinline__ void prefill_tile(
     const uint8_t* __restrict__ A, const float* __restrict__ ASGT, int M, int K,
     const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe, const u32x4* __restrict__ zpa,
@@ -586,7 +608,8 @@ __device__ __forceinline__ void prefill_tile(
 #pragma unroll
     for (int nf = 0; nf < NF; ++nf) {
       bf[nf] = unpack_codes(*reinterpret_cast<const u32x4*>(st + TL::kOffB + (wn * NF + nf) * 1024 + lane * 16));
-      s9[nf] = f16_to_f32(*reinterpret_cast<const uint32_t*>(st + TL::kOffSz + (wn * NF * 16 + 16 * nf + col) * 4)) * 512.0f;
+      s9[nf] = f16_to_f32(*reinterpret_cast<const uint32_t*>(st + TL::kOffSz + (wn * NF * 16 + 16 * nf + col) * 4)) *
+               (kI8 ? 1.0f : 512.0f);   // e4m3 products carry 2^-9 per weight code
     }
     // fragment lane l: row l%16 of the 16-row block, k chunks 2(l/16) and 2(l/16)+1, swizzled
     const int arow = lane & 15, ac0 = 2 * (lane >> 4), asw = arow >> 1;
@@ -604,7 +627,7 @@ __device__ __forceinline__ void prefill_tile(
         if constexpr (!kTok)
           asb[mf & 1] = *reinterpret_cast<const float4*>(st + TL::kOffAsg + (wm * MF * 16 + 16 * mf + 4 * kq) * 4);
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) Tb[mf & 1][nf] = mfma_fp8(a, bf[nf]);
+        for (int nf = 0; nf < NF; ++nf) Tb[mf & 1][nf] = group_product<kI8>(a, bf[nf]);
       }
       if (mf > 0) {
         const int pm = mf - 1;
@@ -714,7 +737,7 @@ struct PrefillMap {
   int wide;      // 1: 256x256 tiles, 0: 128x128 tiles
 };
 
-template <bool kTok>
+template <bool kTok, bool kI8>
 __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ ASGT, int M, int K,
     const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe, const u32x4* __restrict__ zpa,
@@ -736,13 +759,13 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
   if (m0 >= M || n0 >= N) return;   // a piece wholly past the matrix
   const int p = (n0 >= pb1) + (n0 >= pb2);
   if (map.wide) {
-    if (split == 1) prefill_tile<256, 256, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else if (split == 2) prefill_tile<128, 256, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else if (split == 4) prefill_tile<128, 128, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (split == 1) prefill_tile<256, 256, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 2) prefill_tile<128, 256, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 4) prefill_tile<128, 128, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
   } else {
-    if (split == 1) prefill_tile<128, 128, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4, kTok>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (split == 1) prefill_tile<128, 128, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
   }
 }
 
@@ -841,7 +864,7 @@ namespace pq {
 
 // The GEMM behind pq_gemm (kTok = false: a_scale = ASG [P, M, G]) and pq_gemm_tok (kTok = true:
 // a_scale = AS [P, M]); validation is the caller's.
-template <bool kTok>
+template <bool kTok, bool kI8>
 static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scale, const float* rs_d, int M, int K,
                        int P, const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
                        int64_t ldy, void* ws_d, hipStream_t s) {
@@ -860,7 +883,7 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
     }
     DecodeMap map;
     decode_map(N, pb1, pb2, cu_count(), &map);
-    hipLaunchKernelGGL(gemm_decode_kernel, dim3(map.wg0[3]), dim3(64 * kDecWaves), 0, s,
+    hipLaunchKernelGGL(gemm_decode_kernel<kI8>, dim3(map.wg0[3]), dim3(64 * kDecWaves), 0, s,
                        a_d, asg, rs_d, M, K, wpk, sz, N, map, y_d, ldy);
     return launch_status(what);
   }
@@ -883,7 +906,8 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
                      a_scale, rs_d, M, G, P, zpa, asgt);
   // 16-byte output stores need a 16-byte aligned y and a row pitch of 8 elements
   const bool vec16 = aligned(y_d, 16) && ldy % 8 == 0;
-  hipLaunchKernelGGL(gemm_prefill_kernel<kTok>, dim3(static_cast<unsigned>(grid)), dim3(64 * kPfWaves), 0, s,
+  auto prefill = gemm_prefill_kernel<kTok, kI8>;
+  hipLaunchKernelGGL(prefill, dim3(static_cast<unsigned>(grid)), dim3(64 * kPfWaves), 0, s,
                      a_d, kTok ? a_scale : asgt, M, K, wpk, zpe, zpa, sz, N, pb1, pb2, y_d, ldy, map, vec16);
   return launch_status(what);
 }
@@ -920,7 +944,7 @@ int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, in
   const int rc = gemm_check("pq_gemm", a_d, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d, ws_bytes,
                             pq_gemm_workspace_bytes(M, N, K));
   if (rc != PQ_OK) return rc == 1 ? PQ_OK : rc;
-  return gemm_launch<false>("pq_gemm", a_d, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
+  return gemm_launch<false, false>("pq_gemm", a_d, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
                             reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -932,8 +956,21 @@ int pq_gemm_tok(const uint8_t* a_d, const float* as_d, const float* rs_d, int M,
   const int rc = gemm_check("pq_gemm_tok", a_d, as_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
                             ws_bytes, pq_gemm_tok_workspace_bytes(M, N, K));
   if (rc != PQ_OK) return rc == 1 ? PQ_OK : rc;
-  return gemm_launch<true>("pq_gemm_tok", a_d, as_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
+  return gemm_launch<true, false>("pq_gemm_tok", a_d, as_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
                            reinterpret_cast<hipStream_t>(stream));
+}
+
+int pq_gemm_i8(const int8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
+               const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+               int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream) {
+  using namespace pq;
+  clear_error();
+  const uint8_t* a8 = reinterpret_cast<const uint8_t*>(a_d);
+  const int rc = gemm_check("pq_gemm_i8", a8, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d, ws_bytes,
+                            pq_gemm_workspace_bytes(M, N, K));
+  if (rc != PQ_OK) return rc == 1 ? PQ_OK : rc;
+  return gemm_launch<false, true>("pq_gemm_i8", a8, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
+                                  reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

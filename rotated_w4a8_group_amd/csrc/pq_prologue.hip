@@ -99,7 +99,9 @@ __device__ __forceinline__ uint4 load_x8(const uint16_t* p) {
   }
 }
 
-template <bool kVec16>
+// kI8: per-group int8 codes instead of e4m3 (scale amax/127, round half to even, clamp to +-127,
+// integer row-sums).
+template <bool kVec16, bool kI8>
 __global__ __launch_bounds__(256) void rotate_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int K, int P,
     const uint2* __restrict__ rec, const uint16_t* __restrict__ cs, uint8_t* __restrict__ A,
@@ -193,6 +195,36 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(
       for (int j = 0; j < 8; ++j) v[q][j] = *reinterpret_cast<const float*>(slot + q * kProQuadBytes + j * 16);
     }
     __builtin_amdgcn_wave_barrier();
+    if constexpr (kI8) {
+#pragma unroll
+      for (int q = 0; q < kProQuads; ++q) {
+        float m = __builtin_fabsf(v[q][0]);
+#pragma unroll
+        for (int j = 1; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[q][j]));
+        const float amax = row_max(m);
+        const float sc8 = amax / 127.0f;        // correctly rounded division
+        const float iv = recip_rn(sc8);
+        int qi[8], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float r = __builtin_rintf(v[q][j] * iv);       // round half to even
+          qi[j] = amax == 0.0f ? 0 : static_cast<int>(__builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f));
+          sum += qi[j];
+        }
+        const uint32_t w0 = (qi[0] & 0xFF) | ((qi[1] & 0xFF) << 8) | ((qi[2] & 0xFF) << 16) | (static_cast<uint32_t>(qi[3]) << 24);
+        const uint32_t w1 = (qi[4] & 0xFF) | ((qi[5] & 0xFF) << 8) | ((qi[6] & 0xFF) << 16) | (static_cast<uint32_t>(qi[7]) << 24);
+        const int units = row_sum(sum);
+        const int m8 = mb + 4 * q + t;
+        if (m8 < m_end) {
+          *reinterpret_cast<uint2*>(A + (out_base + m8) * K + g * 128 + 8 * c) = make_uint2(w0, w1);
+          if (c == 0) {
+            ASG[(out_base + m8) * G + g] = sc8;
+            RS[(out_base + m8) * G + g] = static_cast<float>(units);   // |units| <= 127 * 128: exact
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < kProQuads; ++q) {
       float m = __builtin_fabsf(v[q][0]);
@@ -380,23 +412,18 @@ static int launch_status(const char* what) {
   return PQ_OK;
 }
 
-}  // namespace pq
-
-extern "C" {
-
-int pq_rotate_quant(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const void* rec_d,
-                    const uint16_t* cs_d, uint8_t* a_d, float* asg_d, float* rs_d,
-                    pq_stream_t stream) {
-  using namespace pq;
-  clear_error();
-  if (M < 0) return set_error(PQ_ERR_SHAPE, "pq_rotate_quant: M=%d < 0", M);
-  if (K <= 0 || K % PQ_GROUP || K > (1 << 24)) return set_error(PQ_ERR_SHAPE, "pq_rotate_quant: K=%d must be a positive multiple of 128", K);
-  if (P < 1 || P > PQ_MAX_PARTITIONS) return set_error(PQ_ERR_PARTITION, "pq_rotate_quant: P=%d must be in 1..3", P);
-  if (ldx < K || (ldx & 1)) return set_error(PQ_ERR_SHAPE, "pq_rotate_quant: ldx=%lld must be even and >= K=%d", static_cast<long long>(ldx), K);
+template <bool kI8>
+static int rotate_quant_launch(const char* what, const uint16_t* x_d, int64_t ldx, int M, int K, int P,
+                               const void* rec_d, const uint16_t* cs_d, uint8_t* a_d, float* asg_d, float* rs_d,
+                               pq_stream_t stream) {
+  if (M < 0) return set_error(PQ_ERR_SHAPE, "%s: M=%d < 0", what, M);
+  if (K <= 0 || K % PQ_GROUP || K > (1 << 24)) return set_error(PQ_ERR_SHAPE, "%s: K=%d must be a positive multiple of 128", what, K);
+  if (P < 1 || P > PQ_MAX_PARTITIONS) return set_error(PQ_ERR_PARTITION, "%s: P=%d must be in 1..3", what, P);
+  if (ldx < K || (ldx & 1)) return set_error(PQ_ERR_SHAPE, "%s: ldx=%lld must be even and >= K=%d", what, static_cast<long long>(ldx), K);
   if (M == 0) return PQ_OK;
-  if (!x_d || !rec_d || !cs_d || !a_d || !asg_d || !rs_d) return set_error(PQ_ERR_NULL, "pq_rotate_quant: NULL pointer");
+  if (!x_d || !rec_d || !cs_d || !a_d || !asg_d || !rs_d) return set_error(PQ_ERR_NULL, "%s: NULL pointer", what);
   if (!aligned(x_d, 4) || !aligned(rec_d, 8) || !aligned(cs_d, 4) || !aligned(a_d, 16) || !aligned(asg_d, 4) || !aligned(rs_d, 4))
-    return set_error(PQ_ERR_ALIGN, "pq_rotate_quant: misaligned pointer");
+    return set_error(PQ_ERR_ALIGN, "%s: misaligned pointer", what);
   const int G = K / PQ_GROUP;
   // tokens per wave unit: a multiple of the 8-token step, as few as keep the unit count near
   // kProUnits (short units for small M, at most 256 tokens)
@@ -406,14 +433,34 @@ int pq_rotate_quant(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const
   const int64_t chunks = (M + tok - 1) / tok;
   const int64_t units = chunks * rows;
   const int64_t blocks = (units + kProWaves - 1) / kProWaves;
-  if (units > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "pq_rotate_quant: problem too large");
+  if (units > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "%s: problem too large", what);
   const bool vec16 = aligned(x_d, 16) && (ldx % 8) == 0;
-  auto kern = vec16 ? rotate_quant_kernel<true> : rotate_quant_kernel<false>;
+  auto kern = vec16 ? rotate_quant_kernel<true, kI8> : rotate_quant_kernel<false, kI8>;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), x_d, ldx, M, K, P,
                      static_cast<const uint2*>(rec_d), cs_d, a_d, asg_d, rs_d, tok,
                      static_cast<int>(chunks));
-  return launch_status("pq_rotate_quant");
+  return launch_status(what);
+}
+
+
+}  // namespace pq
+
+extern "C" {
+
+int pq_rotate_quant(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const void* rec_d,
+                    const uint16_t* cs_d, uint8_t* a_d, float* asg_d, float* rs_d,
+                    pq_stream_t stream) {
+  pq::clear_error();
+  return pq::rotate_quant_launch<false>("pq_rotate_quant", x_d, ldx, M, K, P, rec_d, cs_d, a_d, asg_d, rs_d, stream);
+}
+
+int pq_rotate_quant_i8(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const void* rec_d,
+                       const uint16_t* cs_d, int8_t* a_d, float* asg_d, float* rs_d,
+                       pq_stream_t stream) {
+  pq::clear_error();
+  return pq::rotate_quant_launch<true>("pq_rotate_quant_i8", x_d, ldx, M, K, P, rec_d, cs_d,
+                                       reinterpret_cast<uint8_t*>(a_d), asg_d, rs_d, stream);
 }
 
 int pq_rotate_quant_tok(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const void* rec_d,
