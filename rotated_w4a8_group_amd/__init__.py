@@ -95,6 +95,15 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _nbytes(t):
+    """Size in bytes of an optional workspace tensor (0 for None); the library checks it."""
+    if t is None:
+        return 0
+    if not t.is_cuda or not t.is_contiguous():
+        raise TypeError("workspace: expected a contiguous CUDA tensor")
+    return t.numel() * t.element_size()
+
+
 def _need(t, dtype, name):
     import torch
     if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
@@ -195,7 +204,7 @@ def gemm(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, wor
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
     _check("pq_gemm", lib().pq_gemm(
         _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2,
-        _ptr(out), out.stride(0), _ptr(workspace), ws_bytes if workspace is not None else 0, _stream(stream)))
+        _ptr(out), out.stride(0), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return out
 
 
@@ -239,7 +248,7 @@ def gemm_i8(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, 
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
     _check("pq_gemm_i8", lib().pq_gemm_i8(
         _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2,
-        _ptr(out), out.stride(0), _ptr(workspace), ws_bytes if workspace is not None else 0, _stream(stream)))
+        _ptr(out), out.stride(0), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return out
 
 
@@ -287,7 +296,7 @@ def gemm_tok(A, AS, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, 
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
     _check("pq_gemm_tok", lib().pq_gemm_tok(
         _ptr(A), _ptr(AS), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2,
-        _ptr(out), out.stride(0), _ptr(workspace), ws_bytes if workspace is not None else 0, _stream(stream)))
+        _ptr(out), out.stride(0), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return out
 
 

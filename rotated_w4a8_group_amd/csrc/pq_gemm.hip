@@ -444,7 +444,8 @@ int decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
 // form a WM x WN grid of (TM/WM) x (TN/WN) blocks; one 128-group per k-step. Operands move
 // global -> LDS by direct LDS loads through a 3-stage ring (2 groups ahead). The activation slab
 // arrives as whole 128-byte rows (8 rows per load, fully used cache lines) with the 16-byte chunk
-// index XOR-swizzled by (row/2)%8, which keeps the fragment reads free of bank conflicts; the
+// index XOR-swizzled by (row%8) ^ ((row/8)%2): each 16-lane quarter of a fragment read then
+// covers the 64 LDS banks once (measured on gfx950: (row/2)%8 and row%8 read ~40% slower); the
 // weight image is already in fragment order (each lane reads 16 contiguous bytes). Per group and wave the
 // products T = MFMA(A_g, codes_g) are folded as acc += (asg * 512 sc) * T (2 VALU per output),
 // each row fragment's products issued before the previous fragment's fold. After the loop the
@@ -554,7 +555,7 @@ __device__ __forceinline__ void prefill_tile(
       const int r = 8 * d + (lane >> 3);                 // tile row; lane%8 = chunk slot
       const int row = min(m0 + r, M - 1);
       sbase[i] = Ap;
-      voff[i] = static_cast<uint32_t>(row * K + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+      voff[i] = static_cast<uint32_t>(row * K + 16 * ((lane & 7) ^ (r & 7) ^ ((r >> 3) & 1)));
       step[i] = 128; dst[i] = TL::kOffA + d * 1024; wide[i] = true;
     } else if (d < TL::nA + TL::nB) {
       const int j = d - TL::nA;
@@ -612,7 +613,7 @@ __device__ __forceinline__ void prefill_tile(
                (kI8 ? 1.0f : 512.0f);   // e4m3 products carry 2^-9 per weight code
     }
     // fragment lane l: row l%16 of the 16-row block, k chunks 2(l/16) and 2(l/16)+1, swizzled
-    const int arow = lane & 15, ac0 = 2 * (lane >> 4), asw = arow >> 1;
+    const int arow = lane & 15, ac0 = 2 * (lane >> 4), asw = (arow & 7) ^ (arow >> 3);
     const int aoff0 = arow * 128 + 16 * (ac0 ^ asw), aoff1 = arow * 128 + 16 * ((ac0 + 1) ^ asw);
     // the products of row fragment mf are issued before the fold of mf-1
     v4f Tb[2][NF];

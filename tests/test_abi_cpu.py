@@ -152,7 +152,7 @@ FAKE = ctypes.c_void_p(0x100000)   # aligned, never dereferenced: validation fai
 
 def _gemm(**kw):
     a = dict(a=FAKE, asg=FAKE, rs=FAKE, M=4, K=256, P=1, wpk=FAKE, sz=FAKE, N=128,
-             pb1=pq.NO_BOUNDARY, pb2=pq.NO_BOUNDARY, y=FAKE, ldy=128, ws=None, ws_bytes=0, s=None)
+             pb1=pq.NO_BOUNDARY, pb2=pq.NO_BOUNDARY, y=FAKE, ldy=128, ws=FAKE, ws_bytes=1 << 24, s=None)
     a.update(kw)
     return pq.lib().pq_gemm(a["a"], a["asg"], a["rs"], a["M"], a["K"], a["P"], a["wpk"], a["sz"],
                             a["N"], a["pb1"], a["pb2"], a["y"], a["ldy"], a["ws"], a["ws_bytes"], a["s"])
