@@ -14,10 +14,13 @@ from the page "ParoQuant (PARO) W4A8 on gfx1201 — engineering log" (sections "
 * ``prologue`` — channel scale, 8 rotation layers, per-(token, group) amax, e4m3 encode,
   code-domain row-sums, emulated step by step in IEEE binary32.
 * ``gemm``     — the same-codes reference GEMM, exact per group in fp64.
+* ``tokquant`` — the per-token activation-scale prologue and GEMM.
+* ``int8``     — the per-group int8 activation prologue and GEMM.
+* ``int5``     — the int5 bit-plane weight unpack and GEMM.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against values that do not come
 from the oracle itself (closed forms, library routines, exact rationals, brute force).
 """
-from . import e4m3, awq, records, prologue, gemm  # noqa: F401
+from . import e4m3, awq, records, prologue, gemm, tokquant, int8, int5  # noqa: F401
 
-__all__ = ["e4m3", "awq", "records", "prologue", "gemm"]
+__all__ = ["e4m3", "awq", "records", "prologue", "gemm", "tokquant", "int8", "int5"]

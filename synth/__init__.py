@@ -142,6 +142,40 @@ def weights(wl: Workload) -> Weights:
     return Weights(codes, zp, scales, awq_pack(codes), awq_pack(zp))
 
 
+def bitplane_pack(bits: np.ndarray) -> np.ndarray:
+    """uint8 bits [R, N] (0/1) -> int32 words [R, N/32]: bit j of word w holds column 32w + j
+    (the int5 checkpoint's fifth-bit plane)."""
+    bits = np.asarray(bits, dtype=np.uint32) & 1
+    R, N = bits.shape
+    assert N % 32 == 0
+    w = np.zeros((R, N // 32), dtype=np.uint32)
+    for j in range(32):
+        w |= bits[:, j::32] << np.uint32(j)
+    return w.view(np.int32)
+
+
+@dataclass
+class Weights5:
+    codes: np.ndarray      # uint8 [K, N] 0..31
+    zp: np.ndarray         # uint8 [G, N] 4..28
+    scales: np.ndarray     # f16 [G, N] ~ U(0.001, 0.01)
+    qweight: np.ndarray    # int32 [K, N/8]   low four bits, AWQ order
+    qweight_hi: np.ndarray  # int32 [K, N/32] fifth bits
+    qzeros: np.ndarray     # int32 [G, N/8]
+    qzeros_hi: np.ndarray  # int32 [G, N/32]
+
+
+def weights5(wl: Workload) -> Weights5:
+    """int5 bit-plane weights: codes ~ U{0..31}, zero points ~ U{4..28}, scales ~ U(0.001, 0.01)
+    (half the int4 range, so the dequantised weights span about the same values); the low four
+    bits packed as the int4 checkpoint, the fifth bits as [R, N/32] planes."""
+    codes = rng(wl.wid, T_CODES, 5).integers(0, 32, (wl.K, wl.N), dtype=np.uint8)
+    zp = rng(wl.wid, T_ZP, 5).integers(4, 29, (wl.G, wl.N), dtype=np.uint8)
+    scales = rng(wl.wid, T_SCALES, 5).uniform(0.001, 0.01, (wl.G, wl.N)).astype(np.float16)
+    return Weights5(codes, zp, scales, awq_pack(codes & 15), bitplane_pack(codes >> 4),
+                    awq_pack(zp & 15), bitplane_pack(zp >> 4))
+
+
 def subnormal_heavy_codes(wl: Workload, M: Optional[int] = None):
     """GEMM-only activations with many e4m3 subnormal codes: random codes (finite, not NaN)
     with, in 10% of the (row, group) blocks, half of the codes drawn from 0x01-0x07 /
