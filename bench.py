@@ -46,9 +46,11 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
-def gemm_bytes(M, K, N, P=1):
+def gemm_bytes(M, K, N, P=1, w5=False):
+    """Algorithmic GEMM bytes: packed codes (4 bits per weight, 5 for int5), SZ words,
+    activation codes, scales and row-sums, bf16 output."""
     G = K // 128
-    return K * N // 2 + G * N * 4 + P * M * K + 2 * P * M * G * 4 + M * N * 2
+    return K * N // 2 + (K * N // 8 if w5 else 0) + G * N * 4 + P * M * K + 2 * P * M * G * 4 + M * N * 2
 
 
 def prologue_bytes(M, K, P=1):
@@ -249,6 +251,10 @@ def main():
         for name, key in (("c1_decode_m1", "decode_m1"), ("c3_gate_up_m2048", "prefill"),
                           ("c4_down_m8192", "full_down")):
             out["int8_per_group"][name] = config_measurement(synth.WORKLOADS[key], pq, torch, np, dev, C, i8=True)
+        # int5 bit-plane weights (the e4m3 per-group activations)
+        out["int5_weights"] = {}
+        for name, key in (("c1_decode_m1", "decode_m1"), ("c3_gate_up_m2048", "prefill")):
+            out["int5_weights"][name] = config_measurement(synth.WORKLOADS[key], pq, torch, np, dev, C, w5=True)
         if not args.no_cpu_baseline:
             for name, key in (("c2_qkv_m4_p3", "qkv"), ("c4_gate_up_m8192", "full_gate_up"),
                               ("c4_down_m8192", "full_down")):
@@ -269,7 +275,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False):
+def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False, w5=False):
     """Prologue and GEMM of one workload timed separately: per-launch averages of HIP graphs that
     cycle through weight and activation copies when the call is short (M <= 16), else HIP events
     around eager calls alternating two copies (one such call streams far more than the 256 MB
@@ -280,12 +286,17 @@ def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False):
     C = copies if short else 2
     x0 = synth.activations(wl)
     pl, tl, cl = synth.rotations(wl)
-    w = synth.weights(wl)
     rec = torch.from_numpy(np.stack([pq.build_records(p, t) for p, t in zip(pl, tl)])).to(dev)
     cs = torch.from_numpy(np.stack(cl)).to(dev)
     xs = [torch.from_numpy(x0).to(dev) for _ in range(C)]
-    wq0 = pq.pack_weights(torch.from_numpy(w.qweight).to(dev), torch.from_numpy(w.qzeros).to(dev),
-                          torch.from_numpy(w.scales).to(dev))
+    if w5:
+        w = synth.weights5(wl)
+        wq0 = pq.pack_weights5(*[torch.from_numpy(t).to(dev) for t in (w.qweight, w.qweight_hi, w.qzeros,
+                                                                         w.qzeros_hi, w.scales)])
+    else:
+        w = synth.weights(wl)
+        wq0 = pq.pack_weights(torch.from_numpy(w.qweight).to(dev), torch.from_numpy(w.qzeros).to(dev),
+                              torch.from_numpy(w.scales).to(dev))
     wq = [wq0] + [(wq0[0].clone(), wq0[1].clone()) for _ in range(C - 1)]
     A = torch.empty((P, M, K), dtype=torch.int8 if i8 else torch.uint8, device=dev)
     S = torch.empty((P, M) if tok else (P, M, G), dtype=torch.float32, device=dev)
@@ -299,6 +310,10 @@ def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False):
         ws = torch.empty(max(1, pq.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
         pro = lambda i: pq.rotate_quant_i8(xs[i % C], rec, cs, out=(A, S, R))
         gem = lambda i: pq.gemm_i8(A, S, R, wq[i % C][0], wq[i % C][1], N, *wl.bounds, out=y, workspace=ws)
+    elif w5:
+        ws = torch.empty(max(1, pq.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
+        pro = lambda i: pq.rotate_quant(xs[i % C], rec, cs, out=(A, S, R))
+        gem = lambda i: pq.gemm5(A, S, R, wq[i % C][0], wq[i % C][1], N, *wl.bounds, out=y, workspace=ws)
     else:
         ws = torch.empty(max(1, pq.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
         pro = lambda i: pq.rotate_quant(xs[i % C], rec, cs, out=(A, S, R))
@@ -333,7 +348,7 @@ def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False):
     t_pro = timed(pro, 5 if short else 6)
     t_gem = timed(gem, 5 if short else 6)
     flops = 2.0 * M * N * K
-    gb = gemm_bytes(M, K, N, P)
+    gb = gemm_bytes(M, K, N, P, w5=w5)
     res = {"M": M, "K": K, "N": N, "partitions": P,
            "prologue_us": round(t_pro * 1e6, 2),
            "prologue_GBs": round(prologue_bytes(M, K, P) / t_pro / 1e9, 1),

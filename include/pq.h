@@ -205,6 +205,40 @@ int pq_gemm_i8(const int8_t* a_d, const float* asg_d, const float* rs_d, int M, 
                int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream);
 
 /*
+ * int5 bit-plane weights (W5A8): 5-bit asymmetric codes c in 0..31 per 128-group with zero points
+ * in 0..31 and f16 scales, W = sc * (c - zp); the activations and the GEMM are those of
+ * pq_rotate_quant / pq_gemm. The matrix core takes c - 16, exact in e4m3 for every code.
+ * Source: "2026-09-10: int5 W5A8 ParoQuant -- round-to-nearest checkpoint, kernel and first
+ * served numbers" (the "int5-bitplane" checkpoint: the low four bits in the int4 AWQ words, the
+ * fifth bits in [K, N/32] int32 planes; the int4 path's algebra and zero-point fold carry over).
+ *
+ * pq_pack_weights5 (device, load time):
+ *   qweight_d int32 [K, N/8], qzeros_d int32 [K/128, N/8]: the codes' and zero points' low four
+ *             bits in the AWQ layout of pq_pack_weights.
+ *   qweight_hi_d int32 [K, N/32], qzeros_hi_d int32 [K/128, N/32]: fifth bits; bit j of word w
+ *             is column 32w + j.
+ *   scales_d  f16 [K/128, N].
+ *   wpk5_d    out, pq_packed_weight5_bytes(K, N) bytes: the K*N/2-byte nibble image of
+ *             pq_pack_weights, then K*N/8 bytes of fifth bits in fragment order (256 bytes per
+ *             16 columns x 128-group: lane l's 32-bit word carries the bits of its 32 codes),
+ *             then the zero-point epilogue operand built from sc * (zp - 16).
+ *   sz_d      out, f16 [K/128, N, 2]: {sc, fl16(sc * (zp - 16))}.
+ *   Requires K % 128 == 0, N % 32 == 0, 16-byte aligned wpk5_d, 4-byte aligned others. Returns
+ *   0 bytes from pq_packed_weight5_bytes for shapes the library rejects.
+ * pq_gemm5: arguments as pq_gemm with wpk5_d/sz_d from pq_pack_weights5 (N % 32 == 0):
+ *   y[m, n] = bf16_rne( sum_g asg_p[m,g] * ( sc[g,n] * sum_{k in g} D(A_p[m,k]) * (c[k,n] - 16)
+ *                                            - fl16(sc[g,n]*(zp[g,n]-16)) * rs_p[m,g] ) )
+ *   Same workspace as pq_gemm (pq_gemm_workspace_bytes); M > 16 runs 128x128 tiles.
+ */
+size_t pq_packed_weight5_bytes(int K, int N);
+int pq_pack_weights5(const int32_t* qweight_d, const int32_t* qweight_hi_d, const int32_t* qzeros_d,
+                     const int32_t* qzeros_hi_d, const uint16_t* scales_d, int K, int N, void* wpk5_d,
+                     uint16_t* sz_d, pq_stream_t stream);
+int pq_gemm5(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
+             const void* wpk5_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+             int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream);
+
+/*
  * Verification hooks: run the exact device arithmetic the prologue uses on plain arrays, so
  * tests can check it exhaustively.
  *  pq_e4m3_encode: codes_d[i] = E(q_d[i]) with the prologue's encoder (n >= 0).

@@ -51,6 +51,9 @@ SIGNATURES = {
     "pq_gemm_tok": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
     "pq_rotate_quant_i8": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "pq_gemm_i8": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
+    "pq_packed_weight5_bytes": (_SZ, [_I, _I]),
+    "pq_pack_weights5": (_I, [_P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
+    "pq_gemm5": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
     "pq_e4m3_encode": (_I, [_P, _P, _I64, _P]),
     "pq_recip_f32": (_I, [_P, _P, _I64, _P]),
 }
@@ -159,6 +162,25 @@ def pack_weights(qweight, qzeros, scales, stream=None):
     return wpk, sz
 
 
+def pack_weights5(qweight, qweight_hi, qzeros, qzeros_hi, scales, stream=None):
+    """int5 bit-plane weights: qweight int32 [K, N/8], qweight_hi int32 [K, N/32], qzeros int32
+    [K/128, N/8], qzeros_hi int32 [K/128, N/32], scales f16 [K/128, N] (CUDA)
+    -> (wpk5 uint8 [pq_packed_weight5_bytes], sz f16 [K/128, N, 2])."""
+    import torch
+    for t, name in ((qweight, "qweight"), (qweight_hi, "qweight_hi"), (qzeros, "qzeros"), (qzeros_hi, "qzeros_hi")):
+        _need(t, torch.int32, name)
+    _need(scales, torch.float16, "scales")
+    K, N = qweight.shape[0], qweight.shape[1] * 8
+    if tuple(qweight_hi.shape) != (K, N // 32) or tuple(qzeros_hi.shape) != (K // GROUP, N // 32):
+        raise TypeError("qweight_hi / qzeros_hi: expected [K, N/32] / [K/128, N/32] int32 planes")
+    wpk = torch.empty(max(1, lib().pq_packed_weight5_bytes(K, N)), dtype=torch.uint8, device=qweight.device)
+    sz = torch.empty((K // GROUP, N, 2), dtype=torch.float16, device=qweight.device)
+    _check("pq_pack_weights5", lib().pq_pack_weights5(
+        _ptr(qweight), _ptr(qweight_hi), _ptr(qzeros), _ptr(qzeros_hi), _ptr(scales), K, N,
+        _ptr(wpk), _ptr(sz), _stream(stream)))
+    return wpk, sz
+
+
 def rotate_quant(x, rec, cs, out=None, stream=None):
     """x f16 [M, K] (row stride may exceed K), rec uint8 [P, 8, K/2, 8] (or [8, K/2, 8]),
     cs f16 [P, K] -> (A u8 [P, M, K], ASG f32 [P, M, G], RS f32 [P, M, G])."""
@@ -204,6 +226,28 @@ def gemm(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, wor
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
     _check("pq_gemm", lib().pq_gemm(
         _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2,
+        _ptr(out), out.stride(0), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+    return out
+
+
+def gemm5(A, ASG, RS, wpk5, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, workspace=None, stream=None):
+    """int5 bit-plane weights (from pack_weights5) with the e4m3 prologue's A/ASG/RS -> y bf16 [M, N]."""
+    import torch
+    _need(A, torch.uint8, "A")
+    _need(ASG, torch.float32, "ASG")
+    _need(RS, torch.float32, "RS")
+    _need(wpk5, torch.uint8, "wpk5")
+    _need(sz, torch.float16, "sz")
+    P, M, K = A.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
+        raise TypeError("out: expected a bf16 [M, ldy] tensor with unit column stride")
+    ws_bytes = gemm_workspace_bytes(M, N, K)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
+    _check("pq_gemm5", lib().pq_gemm5(
+        _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk5), _ptr(sz), N, pb1, pb2,
         _ptr(out), out.stride(0), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return out
 

@@ -70,10 +70,46 @@ __device__ __forceinline__ v8i unpack_codes(const u32x4& w) {
   return b;
 }
 
-// {512*sc, 8*sc + zsc} from one SZ word (sc in the low half).
+// int5 weights: the codes' fifth bits ride in a plane beside the nibble image, and the matrix
+// core takes c - 16 as the e4m3 value (c - 16) * 2^-9, exact for every code. With the fifth bit
+// set that is the low nibble's own byte (as in the int4 path); without it the value is negative
+// with magnitude 16 - l, whose e4m3 byte is 0x80 | (16 - l) = 0x90 - l (16 * 2^-9 = 2^-5 is the
+// byte 0x10). Bit 8b + j of a lane's plane word belongs to byte b of operand dword j; v_perm
+// takes each byte from the nibble value (selector 4 + b) or its negative (selector b).
+template <int J>
+__device__ __forceinline__ int w5_dword(uint32_t L, uint32_t H) {
+  const uint32_t hb = (J >= 2 ? (H >> (J - 2)) : (H << (2 - J))) & 0x04040404u;
+  return static_cast<int>(__builtin_amdgcn_perm(L, 0x90909090u - L, 0x03020100u | hb));
+}
+
+__device__ __forceinline__ v8i unpack_codes5(const u32x4& w, uint32_t H) {
+  v8i b;
+  b[0] = w5_dword<0>(w.x & 0x0F0F0F0Fu, H);
+  b[1] = w5_dword<1>((w.x >> 4) & 0x0F0F0F0Fu, H);
+  b[2] = w5_dword<2>(w.y & 0x0F0F0F0Fu, H);
+  b[3] = w5_dword<3>((w.y >> 4) & 0x0F0F0F0Fu, H);
+  b[4] = w5_dword<4>(w.z & 0x0F0F0F0Fu, H);
+  b[5] = w5_dword<5>((w.z >> 4) & 0x0F0F0F0Fu, H);
+  b[6] = w5_dword<6>(w.w & 0x0F0F0F0Fu, H);
+  b[7] = w5_dword<7>((w.w >> 4) & 0x0F0F0F0Fu, H);
+  return b;
+}
+
+// The weight operand of one fragment: int4 nibbles, or nibbles plus the fifth-bit word.
+template <bool kW5>
+__device__ __forceinline__ v8i weight_operand(const u32x4& w, uint32_t H) {
+  if constexpr (kW5) return unpack_codes5(w, H);
+  else return unpack_codes(w);
+}
+
+// {512*sc, zero-point factor} from one SZ word (sc in the low half, zsc in the high half). The
+// product is fed the raw int4 code c (factor 8*sc + zsc = sc * zp, zsc = sc * (zp - 8)) or the
+// signed int5 code c - 16 (factor zsc = sc * (zp - 16)).
+template <bool kW5 = false>
 __device__ __forceinline__ float2 sz_factors(uint32_t w) {
   const float sc = f16_to_f32(w), zsc = f16_to_f32(w >> 16);
-  return make_float2(sc * 512.0f, __builtin_fmaf(sc, 8.0f, zsc));
+  if constexpr (kW5) return make_float2(sc * 512.0f, zsc);
+  else return make_float2(sc * 512.0f, __builtin_fmaf(sc, 8.0f, zsc));
 }
 
 // column n -> nibble position inside its AWQ word (inverse of the order 0,2,4,6,1,3,5,7)
@@ -121,6 +157,45 @@ __global__ void pack_sz_kernel(const int32_t* __restrict__ qzeros, const uint16_
   sz[idx] = static_cast<uint32_t>(sc) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zsc)) << 16);
 }
 
+// int5 fifth-bit plane image: per (16-column tile t, group g) 64 lanes x 4 B; bit 8b + j of lane
+// l's word is the fifth bit of the code at k = 128g + 32(l/16) + 4j + b, column 16t + l%16 (the
+// k of byte b of dword j of the lane's weight operand). One thread per word.
+__global__ void pack_hi_kernel(const int32_t* __restrict__ qweight_hi, int K, int N, uint32_t* __restrict__ hi) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int G = K >> 7;
+  if (idx >= static_cast<int64_t>(N / 16) * G * 64) return;
+  const int l = static_cast<int>(idx & 63);
+  const int64_t rest = idx >> 6;
+  const int t = static_cast<int>(rest / G), g = static_cast<int>(rest % G);
+  const int n = 16 * t + (l & 15);
+  const int k0 = 128 * g + 32 * (l >> 4);
+  const int64_t N32 = N / 32;
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t bit = (static_cast<uint32_t>(qweight_hi[static_cast<int64_t>(k0 + 4 * j + b) * N32 + n / 32]) >> (n & 31)) & 1u;
+      word |= bit << (8 * b + j);
+    }
+  hi[idx] = word;
+}
+
+// SZ words of int5 weights: {sc, fl16(sc * (zp - 16))}, zp = low nibble + 16 * fifth bit; the
+// product sc * (zp - 16) is exact in fp32 (11 x 5 significand bits), rounded once to f16.
+__global__ void pack_sz5_kernel(const int32_t* __restrict__ qzeros, const int32_t* __restrict__ qzeros_hi,
+                                const uint16_t* __restrict__ scales, int G, int N, uint32_t* __restrict__ sz) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(G) * N) return;
+  const int g = static_cast<int>(idx / N), n = static_cast<int>(idx % N);
+  const uint32_t lo = (static_cast<uint32_t>(qzeros[static_cast<int64_t>(g) * (N / 8) + n / 8]) >> awq_shift(n)) & 0xFu;
+  const uint32_t h5 = (static_cast<uint32_t>(qzeros_hi[static_cast<int64_t>(g) * (N / 32) + n / 32]) >> (n & 31)) & 1u;
+  const int zp = static_cast<int>(lo + 16 * h5);
+  const uint16_t sc = scales[idx];
+  const _Float16 zsc = static_cast<_Float16>(f16_to_f32(sc) * static_cast<float>(zp - 16));
+  sz[idx] = static_cast<uint32_t>(sc) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zsc)) << 16);
+}
+
 // ---------------------------------------------------------------------------------------
 // zero-point epilogue operand (load time). The prefill kernel moves the zero-point term
 //   Z[m, n] = sum_g (asg * rs)[m, g] * (8 sc + zsc)[g, n]
@@ -134,6 +209,7 @@ __host__ __device__ constexpr int zpe_chunks(int G) { return (3 * G + 31) / 32; 
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, (h & 0xFFFFu) << 16); }
 
+template <bool kW5>
 __global__ void pack_zpe_kernel(const uint32_t* __restrict__ sz, int G, int N, u32x4* __restrict__ zpe) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int KC = zpe_chunks(G);
@@ -149,7 +225,7 @@ __global__ void pack_zpe_kernel(const uint32_t* __restrict__ sz, int G, int N, u
     uint32_t v = 0;
     if (kp < 3 * G) {
       const int piece = kp / G, g = kp % G;
-      const float2 f = sz_factors(sz[static_cast<size_t>(g) * N + n]);
+      const float2 f = sz_factors<kW5>(sz[static_cast<size_t>(g) * N + n]);
       const uint32_t z1 = f32_to_bf16(f.y);
       v = (piece == 1) ? f32_to_bf16(f.y - bf16_to_f32(z1)) : z1;
     }
@@ -274,25 +350,28 @@ struct DecodeMap {
   int nt[3];    // tiles of partition q
 };
 
-template <int NT>
+constexpr int kDecMaxNT5 = 5;          // int5: six tiles and their planes leave no room for two slots
+template <int NT, bool kW5 = false>
 struct DecodeSlot {
   static constexpr int kSzLoads = (NT + 3) / 4;                 // 64 SZ words per load
   static constexpr int kOffA = NT * 1024;                       // [2 halves][64 lanes][16 B]
   static constexpr int kOffSz = (NT + 2) * 1024;                // [16 NT] words
   static constexpr int kOffSc = kOffSz + kSzLoads * 256;        // [16] asg, [16] rs
-  static constexpr int kBytes = kOffSc + 128;
+  static constexpr int kOffH = kOffSc + 128;                    // int5: [NT][64 lanes] fifth-bit words
+  static constexpr int kBytes = kOffH + (kW5 ? NT * 256 : 0);
   static constexpr int kDepth = kDecRingBytes / kBytes > 16 ? 16 : kDecRingBytes / kBytes;
-  static constexpr int kLoads = NT + 2 + kSzLoads + 2;          // loads per group
+  static constexpr int kLoads = NT + 2 + kSzLoads + 2 + (kW5 ? NT : 0);   // loads per group
   static_assert(kDepth >= 2 && (kDepth - 1) * kLoads <= 63, "decode ring does not fit vmcnt");
 };
 
 // MR = activation rows held per lane that can be live (1 when M == 1, else 4)
-template <int NT, int MR, bool kI8>
+template <int NT, int MR, bool kI8, bool kW5>
 __device__ __forceinline__ void decode_body(
     const uint8_t* __restrict__ A, const float* __restrict__ asgp, const float* __restrict__ rsp,
-    int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ sz, int N, int p,
-    int tfirst, uint16_t* __restrict__ y, int64_t ldy, uint8_t* smem) {
-  using S = DecodeSlot<NT>;
+    int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ hi,
+    const uint32_t* __restrict__ sz, int N, int p, int tfirst, uint16_t* __restrict__ y, int64_t ldy,
+    uint8_t* smem) {
+  using S = DecodeSlot<NT, kW5>;
   constexpr int D = S::kDepth;
   const int G = K >> 7;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -306,6 +385,7 @@ __device__ __forceinline__ void decode_body(
   // stored; the same holds for scale rows >= M.
   const uint8_t* wbase = reinterpret_cast<const uint8_t*>(wpk) + static_cast<size_t>(tfirst) * G * 1024;
   const uint32_t woff = 16 * lane;
+  const uint8_t* hbase = reinterpret_cast<const uint8_t*>(hi) + static_cast<size_t>(tfirst) * G * 256;
   const bool a_on = col < M;
   const uint8_t* abase = A + static_cast<size_t>(p) * M * K;
   const uint32_t aoff = static_cast<uint32_t>((a_on ? col : 0) * K + 32 * kq);
@@ -322,6 +402,11 @@ __device__ __forceinline__ void decode_body(
     const uint8_t* wg = wbase + static_cast<size_t>(g) * 1024;
 #pragma unroll
     for (int t = 0; t < NT; ++t) lds_dma16_s(wg + static_cast<size_t>(t) * G * 1024, woff, sb + t * 1024);
+    if constexpr (kW5) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        lds_dma4_s(hbase + (static_cast<size_t>(t) * G + g) * 256, 4 * lane, sb + S::kOffH + t * 256);
+    }
     if (a_on) {
       lds_dma16_s(abase + 128 * g, aoff, sb + S::kOffA);
       lds_dma16_s(abase + 128 * g + 16, aoff, sb + S::kOffA + 1024);
@@ -358,9 +443,10 @@ __device__ __forceinline__ void decode_body(
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const u32x4 bw = *reinterpret_cast<const u32x4*>(sp + t * 1024 + 16 * lane);
-      float2 f = sz_factors(*reinterpret_cast<const uint32_t*>(sp + S::kOffSz + 4 * (16 * t + col)));
+      float2 f = sz_factors<kW5>(*reinterpret_cast<const uint32_t*>(sp + S::kOffSz + 4 * (16 * t + col)));
       if constexpr (kI8) f.x *= 0x1p-9f;   // integer products carry no 2^-9
-      const v4f T = group_product<kI8>(av, unpack_codes(bw));
+      const uint32_t hw = kW5 ? *reinterpret_cast<const uint32_t*>(sp + S::kOffH + t * 256 + 4 * lane) : 0u;
+      const v4f T = group_product<kI8>(av, weight_operand<kW5>(bw, hw));
 #pragma unroll
       for (int i = 0; i < MR; ++i) acc[t][i] += as[i] * (f.x * T[i] - f.y * rs[i]);
     }
@@ -384,11 +470,11 @@ __device__ __forceinline__ void decode_body(
   }
 }
 
-template <bool kI8>
+template <bool kI8, bool kW5>
 __global__ __launch_bounds__(64 * kDecWaves, kDecPerCU) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ ASG, const float* __restrict__ RS,
-    int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ sz, int N,
-    DecodeMap map, uint16_t* __restrict__ y, int64_t ldy) {
+    int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ hi,
+    const uint32_t* __restrict__ sz, int N, DecodeMap map, uint16_t* __restrict__ y, int64_t ldy) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kDecLds];
   const int b = blockIdx.x;
   const int q = (b >= map.wg0[1]) + (b >= map.wg0[2]);          // partition
@@ -399,10 +485,12 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecPerCU) void gemm_decode_kernel(
   const size_t MG = static_cast<size_t>(M) * (K >> 7);
   const float* asgp = ASG + q * MG;
   const float* rsp = RS + q * MG;
-#define PQ_DECODE_CASE(n)                                                                      \
-  case n:                                                                                      \
-    if (M == 1) decode_body<n, 1, kI8>(A, asgp, rsp, M, K, wpk, sz, N, q, tfirst, y, ldy, smem);   \
-    else decode_body<n, 4, kI8>(A, asgp, rsp, M, K, wpk, sz, N, q, tfirst, y, ldy, smem);          \
+#define PQ_DECODE_CASE(n)                                                                                     \
+  case n:                                                                                                     \
+    if constexpr (!kW5 || n <= kDecMaxNT5) {                                                                  \
+      if (M == 1) decode_body<n, 1, kI8, kW5>(A, asgp, rsp, M, K, wpk, hi, sz, N, q, tfirst, y, ldy, smem);   \
+      else decode_body<n, 4, kI8, kW5>(A, asgp, rsp, M, K, wpk, hi, sz, N, q, tfirst, y, ldy, smem);          \
+    }                                                                                                         \
     break;
   switch (cnt) {
     PQ_DECODE_CASE(1) PQ_DECODE_CASE(2) PQ_DECODE_CASE(3)
@@ -416,11 +504,11 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecPerCU) void gemm_decode_kernel(
 // workgroup slots (kDecPerCU per CU), each workgroup taking at most kDecMaxNT tiles per round,
 // split over the partitions in proportion to their tiles; returns the largest run of tiles any
 // workgroup gets.
-int decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
+int decode_map(int N, int pb1, int pb2, int cus, int maxnt, DecodeMap* map) {
   const int NTT = N / 16;
   const int tb[4] = {0, pb1 < N ? pb1 / 16 : NTT, pb2 < N ? pb2 / 16 : NTT, NTT};
   const int64_t slots = static_cast<int64_t>(kDecPerCU) * cus;
-  const int64_t rounds = (NTT + kDecMaxNT * slots - 1) / (kDecMaxNT * slots);
+  const int64_t rounds = (NTT + maxnt * slots - 1) / (maxnt * slots);
   const int64_t W = std::min<int64_t>(NTT, rounds * slots);
   int maxrun = 0, wg = 0;
   for (int q = 0; q < 3; ++q) {
@@ -430,7 +518,7 @@ int decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
     map->nt[q] = nt;
     if (nt <= 0) continue;
     int64_t w = (W * nt + NTT / 2) / NTT;
-    w = std::max<int64_t>(w, (nt + kDecMaxNT - 1) / kDecMaxNT);
+    w = std::max<int64_t>(w, (nt + maxnt - 1) / maxnt);
     w = std::min<int64_t>(std::max<int64_t>(w, 1), nt);
     wg += static_cast<int>(w);
     maxrun = std::max(maxrun, static_cast<int>((nt + w - 1) / w));
@@ -461,16 +549,18 @@ constexpr int kPfStages = 3;
 constexpr int kPfWaves = 8;
 constexpr int kPfLds = kPfStages * 51200;   // the 256x256 ring (the largest)
 
-template <int TM, int TN, int WM, int WN, bool kTok = false>
+template <int TM, int TN, int WM, int WN, bool kTok = false, bool kW5 = false>
 struct PfTile {
   static constexpr int MF = TM / WM / 16, NF = TN / WN / 16;   // fragments per wave
   static constexpr int kOffA = 0;                              // [TM rows][8 chunks][16 B], chunks swizzled
   static constexpr int kOffB = TM * 128;                       // [TN/16 tiles][64 lanes][16 B]
   static constexpr int kOffAsg = kOffB + TN * 64;              // [TM] f32
   static constexpr int kOffSz = kOffAsg + TM * 4;              // [TN] u32
-  static constexpr int kStage = (kOffSz + TN * 4 + 255) / 256 * 256;
+  static constexpr int kOffH = kOffSz + TN * 4;                // int5: [TN/16 tiles][64 lanes] u32
+  static constexpr int kStage = (kOffH + (kW5 ? TN * 16 : 0) + 255) / 256 * 256;
   static constexpr int nA = TM / 8, nB = TN / 16, nAs = kTok ? 0 : TM / 64, nSz = TN / 64;
-  static constexpr int nD = nA + nB + nAs + nSz;                // direct loads per group
+  static constexpr int nH = kW5 ? TN / 16 : 0;
+  static constexpr int nD = nA + nB + nAs + nSz + nH;          // direct loads per group
   static constexpr int kPerWave = (nD + 3) / 4;                 // loads per wave of the issuing half
   static constexpr int kOutStride = TN + 8;                    // bf16 per staged output row
   static_assert(WM * WN == kPfWaves && MF >= 1 && NF >= 1 && TM % 64 == 0 && TN % 64 == 0, "tile");
@@ -518,13 +608,13 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
   return bid < 8 * q ? (bid % 8) * q + bid / 8 : bid;
 }
 
-template <int TM, int TN, int WM, int WN, bool kTok, bool kI8>
+template <int TM, int TN, int WM, int WN, bool kTok, bool kI8, bool kW5>
 __device__ __forceinline__ void prefill_tile(
     const uint8_t* __restrict__ A, const float* __restrict__ ASGT, int M, int K,
-    const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe, const u32x4* __restrict__ zpa,
-    const uint32_t* __restrict__ sz, int N, int p, int m0, int n0, uint16_t* __restrict__ y,
-    int64_t ldy, bool vec16, uint8_t* smem) {
-  using TL = PfTile<TM, TN, WM, WN, kTok>;
+    const u32x4* __restrict__ wpk, const uint32_t* __restrict__ hi, const u32x4* __restrict__ zpe,
+    const u32x4* __restrict__ zpa, const uint32_t* __restrict__ sz, int N, int p, int m0, int n0,
+    uint16_t* __restrict__ y, int64_t ldy, bool vec16, uint8_t* smem) {
+  using TL = PfTile<TM, TN, WM, WN, kTok, kW5>;
   constexpr int MF = TL::MF, NF = TL::NF, PW = TL::kPerWave;
   const int G = K >> 7;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -568,11 +658,17 @@ __device__ __forceinline__ void prefill_tile(
       sbase[i] = reinterpret_cast<const uint8_t*>(asgp);
       voff[i] = static_cast<uint32_t>(min(m0 + 64 * j + lane, M - 1) * 4);
       step[i] = static_cast<size_t>(M) * 4; dst[i] = TL::kOffAsg + j * 256; wide[i] = false;
-    } else {
+    } else if (d < TL::nA + TL::nB + TL::nAs + TL::nSz) {
       const int j = d - TL::nA - TL::nB - TL::nAs;
       sbase[i] = reinterpret_cast<const uint8_t*>(sz);
       voff[i] = static_cast<uint32_t>(min(n0 + 64 * j + lane, N - 1) * 4);
       step[i] = static_cast<size_t>(N) * 4; dst[i] = TL::kOffSz + j * 256; wide[i] = false;
+    } else {
+      const int j = d - TL::nA - TL::nB - TL::nAs - TL::nSz;   // int5 fifth-bit words of tile j
+      const int tt = min(n0 / 16 + j, last_tile);
+      sbase[i] = reinterpret_cast<const uint8_t*>(hi) + static_cast<size_t>(tt) * G * 256;
+      voff[i] = 4 * lane;
+      step[i] = 256; dst[i] = TL::kOffH + j * 256; wide[i] = false;
     }
   }
   const uint32_t lds0 = lds_addr(smem);
@@ -608,7 +704,8 @@ __device__ __forceinline__ void prefill_tile(
     float s9[NF];
 #pragma unroll
     for (int nf = 0; nf < NF; ++nf) {
-      bf[nf] = unpack_codes(*reinterpret_cast<const u32x4*>(st + TL::kOffB + (wn * NF + nf) * 1024 + lane * 16));
+      const uint32_t hw = kW5 ? *reinterpret_cast<const uint32_t*>(st + TL::kOffH + (wn * NF + nf) * 256 + lane * 4) : 0u;
+      bf[nf] = weight_operand<kW5>(*reinterpret_cast<const u32x4*>(st + TL::kOffB + (wn * NF + nf) * 1024 + lane * 16), hw);
       s9[nf] = f16_to_f32(*reinterpret_cast<const uint32_t*>(st + TL::kOffSz + (wn * NF * 16 + 16 * nf + col) * 4)) *
                (kI8 ? 1.0f : 512.0f);   // e4m3 products carry 2^-9 per weight code
     }
@@ -738,12 +835,12 @@ struct PrefillMap {
   int wide;      // 1: 256x256 tiles, 0: 128x128 tiles
 };
 
-template <bool kTok, bool kI8>
+template <bool kTok, bool kI8, bool kW5>
 __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ ASGT, int M, int K,
-    const u32x4* __restrict__ wpk, const u32x4* __restrict__ zpe, const u32x4* __restrict__ zpa,
-    const uint32_t* __restrict__ sz, int N, int pb1, int pb2, uint16_t* __restrict__ y, int64_t ldy,
-    PrefillMap map, bool vec16) {
+    const u32x4* __restrict__ wpk, const uint32_t* __restrict__ hi, const u32x4* __restrict__ zpe,
+    const u32x4* __restrict__ zpa, const uint32_t* __restrict__ sz, int N, int pb1, int pb2,
+    uint16_t* __restrict__ y, int64_t ldy, PrefillMap map, bool vec16) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfLds];
   const int b = blockIdx.x;
   const int bt = map.wide ? 256 : 128;
@@ -759,14 +856,17 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
   else if (split == 8) { m0 += 64 * (r & 3); n0 += 128 * (r >> 2); }
   if (m0 >= M || n0 >= N) return;   // a piece wholly past the matrix
   const int p = (n0 >= pb1) + (n0 >= pb2);
-  if (map.wide) {
-    if (split == 1) prefill_tile<256, 256, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else if (split == 2) prefill_tile<128, 256, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else if (split == 4) prefill_tile<128, 128, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+  // int5 runs 128x128 tiles only: its fifth-bit planes do not fit three 256x256 stages in LDS
+  if (!kW5 && map.wide) {
+    if constexpr (!kW5) {
+      if (split == 1) prefill_tile<256, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+      else if (split == 2) prefill_tile<128, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+      else if (split == 4) prefill_tile<128, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+      else prefill_tile<64, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    }
   } else {
-    if (split == 1) prefill_tile<128, 128, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4, kTok, kI8>(A, ASGT, M, K, wpk, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (split == 1) prefill_tile<128, 128, 2, 4, kTok, kI8, kW5>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4, kTok, kI8, kW5>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
   }
 }
 
@@ -840,9 +940,49 @@ int pq_pack_weights(const int32_t* qweight_d, const int32_t* qzeros_d, const uin
                      qzeros_d, scales_d, G, N, reinterpret_cast<uint32_t*>(sz_d));
   const int64_t zl = static_cast<int64_t>(N / 16) * zpe_chunks(G) * 64;
   u32x4* zpe = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(wpk_d) + static_cast<size_t>(K) * N / 2);
-  hipLaunchKernelGGL(pack_zpe_kernel, dim3(static_cast<unsigned>((zl + 255) / 256)), dim3(256), 0, s,
+  auto zk = pack_zpe_kernel<false>;
+  hipLaunchKernelGGL(zk, dim3(static_cast<unsigned>((zl + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t*>(sz_d), G, N, zpe);
   return launch_status("pq_pack_weights");
+}
+
+size_t pq_packed_weight5_bytes(int K, int N) {
+  if (K <= 0 || N <= 0 || K % PQ_GROUP || N % 32) return 0;
+  const size_t kn = static_cast<size_t>(K) * static_cast<size_t>(N);
+  const size_t zpe = static_cast<size_t>(N / 16) * pq::zpe_chunks(K / PQ_GROUP) * 1024;
+  return kn / 2 + kn / 8 + zpe;
+}
+
+int pq_pack_weights5(const int32_t* qweight_d, const int32_t* qweight_hi_d, const int32_t* qzeros_d,
+                     const int32_t* qzeros_hi_d, const uint16_t* scales_d, int K, int N, void* wpk_d,
+                     uint16_t* sz_d, pq_stream_t stream) {
+  using namespace pq;
+  clear_error();
+  if (K <= 0 || K % PQ_GROUP || K > (1 << 24)) return set_error(PQ_ERR_SHAPE, "pq_pack_weights5: K=%d must be a positive multiple of 128", K);
+  if (N <= 0 || N % 32 || N > (1 << 24)) return set_error(PQ_ERR_SHAPE, "pq_pack_weights5: N=%d must be a positive multiple of 32", N);
+  if (!qweight_d || !qweight_hi_d || !qzeros_d || !qzeros_hi_d || !scales_d || !wpk_d || !sz_d)
+    return set_error(PQ_ERR_NULL, "pq_pack_weights5: NULL pointer");
+  if (!aligned(qweight_d, 4) || !aligned(qweight_hi_d, 4) || !aligned(qzeros_d, 4) || !aligned(qzeros_hi_d, 4) ||
+      !aligned(scales_d, 2) || !aligned(wpk_d, 16) || !aligned(sz_d, 4))
+    return set_error(PQ_ERR_ALIGN, "pq_pack_weights5: misaligned pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int G = K / PQ_GROUP;
+  const int64_t words = static_cast<int64_t>(K) * N / 8;
+  uint8_t* wb = static_cast<uint8_t*>(wpk_d);
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, s,
+                     qweight_d, K, N, reinterpret_cast<uint32_t*>(wb));
+  const int64_t hw = static_cast<int64_t>(N / 16) * G * 64;
+  hipLaunchKernelGGL(pack_hi_kernel, dim3(static_cast<unsigned>((hw + 255) / 256)), dim3(256), 0, s,
+                     qweight_hi_d, K, N, reinterpret_cast<uint32_t*>(wb + static_cast<size_t>(K) * N / 2));
+  const int64_t gn = static_cast<int64_t>(G) * N;
+  hipLaunchKernelGGL(pack_sz5_kernel, dim3(static_cast<unsigned>((gn + 255) / 256)), dim3(256), 0, s,
+                     qzeros_d, qzeros_hi_d, scales_d, G, N, reinterpret_cast<uint32_t*>(sz_d));
+  const int64_t zl = static_cast<int64_t>(N / 16) * zpe_chunks(G) * 64;
+  u32x4* zpe = reinterpret_cast<u32x4*>(wb + static_cast<size_t>(K) * N / 2 + static_cast<size_t>(K) * N / 8);
+  auto zk = pack_zpe_kernel<true>;
+  hipLaunchKernelGGL(zk, dim3(static_cast<unsigned>((zl + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(sz_d), G, N, zpe);
+  return launch_status("pq_pack_weights5");
 }
 
 size_t pq_gemm_workspace_bytes(int M, int N, int K) {
@@ -863,15 +1003,20 @@ size_t pq_gemm_tok_workspace_bytes(int M, int N, int K) {
 
 namespace pq {
 
-// The GEMM behind pq_gemm (kTok = false: a_scale = ASG [P, M, G]) and pq_gemm_tok (kTok = true:
-// a_scale = AS [P, M]); validation is the caller's.
-template <bool kTok, bool kI8>
+// The GEMM behind pq_gemm (kTok = false: a_scale = ASG [P, M, G]), pq_gemm_tok (kTok = true:
+// a_scale = AS [P, M]), pq_gemm_i8 (kI8) and pq_gemm5 (kW5: int5 packed weights); validation is
+// the caller's.
+template <bool kTok, bool kI8, bool kW5 = false>
 static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scale, const float* rs_d, int M, int K,
                        int P, const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
                        int64_t ldy, void* ws_d, hipStream_t s) {
   const int G = K / PQ_GROUP;
   const u32x4* wpk = static_cast<const u32x4*>(wpk_d);
   const uint32_t* sz = reinterpret_cast<const uint32_t*>(sz_d);
+  // packed image: codes (K N / 2 bytes), [int5: fifth-bit planes (K N / 8)], zero-point operand
+  const uint8_t* wb = static_cast<const uint8_t*>(wpk_d);
+  const uint32_t* hi = kW5 ? reinterpret_cast<const uint32_t*>(wb + static_cast<size_t>(K) * N / 2) : nullptr;
+  const u32x4* zpe = reinterpret_cast<const u32x4*>(wb + static_cast<size_t>(K) * N / 2 + (kW5 ? static_cast<size_t>(K) * N / 8 : 0));
   if (M <= 16) {
     const float* asg = a_scale;
     if (kTok) {
@@ -883,13 +1028,15 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
       asg = ex;
     }
     DecodeMap map;
-    decode_map(N, pb1, pb2, cu_count(), &map);
-    hipLaunchKernelGGL(gemm_decode_kernel<kI8>, dim3(map.wg0[3]), dim3(64 * kDecWaves), 0, s,
-                       a_d, asg, rs_d, M, K, wpk, sz, N, map, y_d, ldy);
+    decode_map(N, pb1, pb2, cu_count(), kW5 ? kDecMaxNT5 : kDecMaxNT, &map);
+    auto dec = gemm_decode_kernel<kI8, kW5>;
+    hipLaunchKernelGGL(dec, dim3(map.wg0[3]), dim3(64 * kDecWaves), 0, s,
+                       a_d, asg, rs_d, M, K, wpk, hi, sz, N, map, y_d, ldy);
     return launch_status(what);
   }
   // 256x256 tiles (one workgroup per CU) unless a partition boundary is not on a 256-column line
-  const bool wide = (pb1 >= N || pb1 % 256 == 0) && (pb2 >= N || pb2 % 256 == 0);
+  // or the weights are int5
+  const bool wide = !kW5 && (pb1 >= N || pb1 % 256 == 0) && (pb2 >= N || pb2 % 256 == 0);
   const int bt = wide ? 256 : 128;
   const int64_t tiles = static_cast<int64_t>((M + bt - 1) / bt) * ((N + bt - 1) / bt);
   if (tiles * 8 > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "%s: problem too large", what);
@@ -898,7 +1045,6 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
     return set_error(PQ_ERR_SHAPE, "%s: M * K too large for one call (split the rows)", what);
   const PrefillMap map = prefill_map(M, N, wide, cu_count());
   const int64_t grid = static_cast<int64_t>(map.full) + static_cast<int64_t>(map.ntiles - map.full) * map.split;
-  const u32x4* zpe = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(wpk_d) + static_cast<size_t>(K) * N / 2);
   u32x4* zpa = static_cast<u32x4*>(ws_d);
   float* asgt = kTok ? nullptr
                      : reinterpret_cast<float*>(static_cast<uint8_t*>(ws_d) + zpe_act_bytes(M, G, PQ_MAX_PARTITIONS));
@@ -907,9 +1053,9 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
                      a_scale, rs_d, M, G, P, zpa, asgt);
   // 16-byte output stores need a 16-byte aligned y and a row pitch of 8 elements
   const bool vec16 = aligned(y_d, 16) && ldy % 8 == 0;
-  auto prefill = gemm_prefill_kernel<kTok, kI8>;
+  auto prefill = gemm_prefill_kernel<kTok, kI8, kW5>;
   hipLaunchKernelGGL(prefill, dim3(static_cast<unsigned>(grid)), dim3(64 * kPfWaves), 0, s,
-                     a_d, kTok ? a_scale : asgt, M, K, wpk, zpe, zpa, sz, N, pb1, pb2, y_d, ldy, map, vec16);
+                     a_d, kTok ? a_scale : asgt, M, K, wpk, hi, zpe, zpa, sz, N, pb1, pb2, y_d, ldy, map, vec16);
   return launch_status(what);
 }
 
@@ -959,6 +1105,19 @@ int pq_gemm_tok(const uint8_t* a_d, const float* as_d, const float* rs_d, int M,
   if (rc != PQ_OK) return rc == 1 ? PQ_OK : rc;
   return gemm_launch<true, false>("pq_gemm_tok", a_d, as_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
                            reinterpret_cast<hipStream_t>(stream));
+}
+
+int pq_gemm5(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
+             const void* wpk5_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+             int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream) {
+  using namespace pq;
+  clear_error();
+  if (N % 32) return set_error(PQ_ERR_SHAPE, "pq_gemm5: N=%d must be a multiple of 32", N);
+  const int rc = gemm_check("pq_gemm5", a_d, asg_d, rs_d, M, K, P, wpk5_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d, ws_bytes,
+                            pq_gemm_workspace_bytes(M, N, K));
+  if (rc != PQ_OK) return rc == 1 ? PQ_OK : rc;
+  return gemm_launch<false, false, true>("pq_gemm5", a_d, asg_d, rs_d, M, K, P, wpk5_d, sz_d, N, pb1, pb2, y_d, ldy,
+                                         ws_d, reinterpret_cast<hipStream_t>(stream));
 }
 
 int pq_gemm_i8(const int8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,

@@ -182,6 +182,23 @@ def test_gemm_m0_is_noop_and_partition_ok():
     assert _gemm(M=32, ws=None, ws_bytes=1 << 20) == -1
 
 
+def test_gemm5_and_pack5_validation():
+    lib = pq.lib()
+    # int5 needs N % 32 == 0 (the fifth-bit planes hold 32 columns per word)
+    assert lib.pq_gemm5(FAKE, FAKE, FAKE, 4, 256, 1, FAKE, FAKE, 48, pq.NO_BOUNDARY, pq.NO_BOUNDARY,
+                        FAKE, 48, FAKE, 1 << 24, None) == -2
+    assert lib.pq_gemm5(None, FAKE, FAKE, 4, 256, 1, FAKE, FAKE, 64, pq.NO_BOUNDARY, pq.NO_BOUNDARY,
+                        FAKE, 64, FAKE, 1 << 24, None) == -1
+    assert lib.pq_gemm5(FAKE, FAKE, FAKE, 0, 256, 1, FAKE, FAKE, 64, pq.NO_BOUNDARY, pq.NO_BOUNDARY,
+                        FAKE, 64, FAKE, 1 << 24, None) == 0
+    assert lib.pq_pack_weights5(FAKE, FAKE, FAKE, FAKE, FAKE, 256, 48, FAKE, FAKE, None) == -2
+    assert lib.pq_pack_weights5(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 64, FAKE, FAKE, None) == -2
+    assert lib.pq_pack_weights5(FAKE, None, FAKE, FAKE, FAKE, 256, 64, FAKE, FAKE, None) == -1
+    # nibble image + fifth-bit planes (K N / 8) + zero-point operand
+    assert lib.pq_packed_weight5_bytes(5120, 17408) == 5120 * 17408 // 2 + 5120 * 17408 // 8 + 1088 * 4 * 1024
+    assert lib.pq_packed_weight5_bytes(256, 48) == 0
+
+
 def _rq(**kw):
     a = dict(x=FAKE, ldx=256, M=4, K=256, P=1, rec=FAKE, cs=FAKE, A=FAKE, asg=FAKE, rs=FAKE, s=None)
     a.update(kw)
