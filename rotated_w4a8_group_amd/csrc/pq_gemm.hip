@@ -827,12 +827,16 @@ __device__ __forceinline__ void prefill_tile(
   store_tile_rows<TM, TN, TL::kOutStride>(ot, y, ldy, m0, n0, M, N, vec16);
 }
 
+// Tile shapes of the prefill grid: 256x256 (pieces 128x256, 128x128, 64x128), 128x128 (pieces
+// 64x128) when a partition boundary is not on a 256-column line, and 128x256 for int5 weights
+// (pieces 128x128, 64x128), whose fifth-bit planes do not fit three 256x256 stages in LDS.
+enum PfShape : int { kPfWide = 0, kPfNarrow = 1, kPfFlat = 2 };
 struct PrefillMap {
   int tiles_m;   // whole tiles per tile column
   int ntiles;    // whole tiles
   int full;      // workgroups that run whole tiles (whole rounds); the rest run pieces
-  int split;     // pieces per remaining tile: 1, 2, 4 or 8 (wide) / 1 or 2 (narrow)
-  int wide;      // 1: 256x256 tiles, 0: 128x128 tiles
+  int split;     // pieces per remaining tile: 1, 2, 4 or 8 (wide) / 1 or 2 (narrow) / 1, 2 or 4 (flat)
+  int shape;     // PfShape
 };
 
 template <bool kTok, bool kI8, bool kW5>
@@ -843,21 +847,35 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
     uint16_t* __restrict__ y, int64_t ldy, PrefillMap map, bool vec16) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfLds];
   const int b = blockIdx.x;
-  const int bt = map.wide ? 256 : 128;
+  const int bm = map.shape == kPfWide ? 256 : 128, bn = map.shape == kPfNarrow ? 128 : 256;
   const bool piece = b >= map.full;
   const int big = piece ? map.full + (b - map.full) / map.split : b;
   const int r = piece ? (b - map.full) % map.split : 0;
   const int t = xcd_tile(big, map.ntiles);
-  int m0 = (t % map.tiles_m) * bt, n0 = (t / map.tiles_m) * bt;
+  int m0 = (t % map.tiles_m) * bm, n0 = (t / map.tiles_m) * bn;
   const int split = piece ? map.split : 1;
-  // piece r of a whole tile: split 2 -> 2 row halves; 4 -> 2 x 2 quarters; 8 -> 4 row x 2 column
-  if (split == 2) m0 += (bt / 2) * r;
-  else if (split == 4) { m0 += 128 * (r & 1); n0 += 128 * (r >> 1); }
-  else if (split == 8) { m0 += 64 * (r & 3); n0 += 128 * (r >> 2); }
+  if (map.shape == kPfFlat) {
+    // piece r of a 128x256 tile: split 2 -> 2 column halves; 4 -> 2 row x 2 column
+    if (split == 2) n0 += 128 * r;
+    else if (split == 4) { m0 += 64 * (r & 1); n0 += 128 * (r >> 1); }
+  } else {
+    // piece r of a whole tile: split 2 -> 2 row halves; 4 -> 2 x 2 quarters; 8 -> 4 row x 2 column
+    if (split == 2) m0 += (bm / 2) * r;
+    else if (split == 4) { m0 += 128 * (r & 1); n0 += 128 * (r >> 1); }
+    else if (split == 8) { m0 += 64 * (r & 3); n0 += 128 * (r >> 2); }
+  }
   if (m0 >= M || n0 >= N) return;   // a piece wholly past the matrix
   const int p = (n0 >= pb1) + (n0 >= pb2);
-  // int5 runs 128x128 tiles only: its fifth-bit planes do not fit three 256x256 stages in LDS
-  if (!kW5 && map.wide) {
+  if constexpr (kW5) {
+    if (map.shape == kPfFlat && split == 1)
+      prefill_tile<128, 256, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (map.shape == kPfFlat ? split == 2 : split == 1)
+      prefill_tile<128, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else
+      prefill_tile<64, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    return;
+  }
+  if (map.shape == kPfWide) {
     if constexpr (!kW5) {
       if (split == 1) prefill_tile<256, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
       else if (split == 2) prefill_tile<128, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
@@ -871,22 +889,20 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
 }
 
 // Whole rounds of tiles (one workgroup per CU), then the remaining tiles in pieces.
-PrefillMap prefill_map(int M, int N, bool wide, int cus) {
+PrefillMap prefill_map(int M, int N, int shape, int cus) {
   PrefillMap m{};
-  const int bt = wide ? 256 : 128;
-  m.wide = wide ? 1 : 0;
-  m.tiles_m = (M + bt - 1) / bt;
-  const int64_t nt = static_cast<int64_t>(m.tiles_m) * ((N + bt - 1) / bt);
+  const int bm = shape == kPfWide ? 256 : 128, bn = shape == kPfNarrow ? 128 : 256;
+  m.shape = shape;
+  m.tiles_m = (M + bm - 1) / bm;
+  const int64_t nt = static_cast<int64_t>(m.tiles_m) * ((N + bn - 1) / bn);
   m.ntiles = static_cast<int>(nt);
   const int64_t full = (nt / cus) * cus, rem = nt - full;
   m.full = static_cast<int>(full);
   m.split = 1;
   if (rem > 0) {
-    const int cands_wide[3] = {8, 4, 2}, cands_narrow[1] = {2};
-    const int* c = wide ? cands_wide : cands_narrow;
-    const int nc = wide ? 3 : 1;
-    for (int i = 0; i < nc; ++i)
-      if (rem * c[i] <= cus) { m.split = c[i]; break; }
+    static const int cands[3][3] = {{8, 4, 2}, {2, 0, 0}, {4, 2, 0}};
+    for (int i = 0; i < 3 && cands[shape][i]; ++i)
+      if (rem * cands[shape][i] <= cus) { m.split = cands[shape][i]; break; }
   }
   return m;
 }
@@ -1034,16 +1050,16 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
                        a_d, asg, rs_d, M, K, wpk, hi, sz, N, map, y_d, ldy);
     return launch_status(what);
   }
-  // 256x256 tiles (one workgroup per CU) unless a partition boundary is not on a 256-column line
-  // or the weights are int5
-  const bool wide = !kW5 && (pb1 >= N || pb1 % 256 == 0) && (pb2 >= N || pb2 % 256 == 0);
-  const int bt = wide ? 256 : 128;
-  const int64_t tiles = static_cast<int64_t>((M + bt - 1) / bt) * ((N + bt - 1) / bt);
+  // 256x256 tiles (one workgroup per CU; 128x256 for int5) unless a partition boundary is not on
+  // a 256-column line
+  const bool on256 = (pb1 >= N || pb1 % 256 == 0) && (pb2 >= N || pb2 % 256 == 0);
+  const int shape = !on256 ? kPfNarrow : (kW5 ? kPfFlat : kPfWide);
+  const int64_t tiles = static_cast<int64_t>((M + 127) / 128) * ((N + 127) / 128);
   if (tiles * 8 > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "%s: problem too large", what);
   // the prefill kernel addresses a partition's activations with 32-bit lane offsets
   if (static_cast<int64_t>(M) * K > 0x7FFFFFFF || static_cast<int64_t>(M) * (K / PQ_GROUP) * 4 > 0x7FFFFFFF)
     return set_error(PQ_ERR_SHAPE, "%s: M * K too large for one call (split the rows)", what);
-  const PrefillMap map = prefill_map(M, N, wide, cu_count());
+  const PrefillMap map = prefill_map(M, N, shape, cu_count());
   const int64_t grid = static_cast<int64_t>(map.full) + static_cast<int64_t>(map.ntiles - map.full) * map.split;
   u32x4* zpa = static_cast<u32x4*>(ws_d);
   float* asgt = kTok ? nullptr
