@@ -17,10 +17,11 @@ from the page "ParoQuant (PARO) W4A8 on gfx1201 — engineering log" (sections "
 * ``tokquant`` — the per-token activation-scale prologue and GEMM.
 * ``int8``     — the per-group int8 activation prologue and GEMM.
 * ``int5``     — the int5 bit-plane weight unpack and GEMM.
+* ``producer`` — the fused residual add + RMSNorm + rotate + quant producer.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against values that do not come
 from the oracle itself (closed forms, library routines, exact rationals, brute force).
 """
-from . import e4m3, awq, records, prologue, gemm, tokquant, int8, int5  # noqa: F401
+from . import e4m3, awq, records, prologue, gemm, tokquant, int8, int5, producer  # noqa: F401
 
-__all__ = ["e4m3", "awq", "records", "prologue", "gemm", "tokquant", "int8", "int5"]
+__all__ = ["e4m3", "awq", "records", "prologue", "gemm", "tokquant", "int8", "int5", "producer"]
