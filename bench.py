@@ -251,6 +251,10 @@ def main():
         for name, key in (("c1_decode_m1", "decode_m1"), ("c3_gate_up_m2048", "prefill"),
                           ("c4_down_m8192", "full_down")):
             out["int8_per_group"][name] = config_measurement(synth.WORKLOADS[key], pq, torch, np, dev, C, i8=True)
+        # the fused residual add + RMSNorm + rotate-quant producer against the unfused chain
+        out["fused_producer"] = {}
+        for name, key in (("c1_decode_m1", "decode_m1"), ("c1_decode_m8", "decode_m8"), ("c3_gate_up_m2048", "prefill")):
+            out["fused_producer"][name] = producer_measurement(synth.WORKLOADS[key], pq, torch, np, dev, C)
         # int5 bit-plane weights (the e4m3 per-group activations)
         out["int5_weights"] = {}
         for name, key in (("c1_decode_m1", "decode_m1"), ("c3_gate_up_m2048", "prefill")):
@@ -273,6 +277,69 @@ def main():
                             "gpu_over_oracle": round(wall / ((c3["prologue_us"] + c3["gemm_us"]) * 1e-6), 1)}
 
     print(json.dumps(out), flush=True)
+
+
+def producer_measurement(wl, pq, torch, np, dev, copies):
+    """pq_add_rms_rotate_quant against the unfused chain (torch add, torch rms_norm in float32 with
+    the Gemma 1 + w weight, pq_rotate_quant): per-launch averages of HIP graphs over `copies` input
+    copies when M <= 16, else HIP events around eager calls alternating two copies."""
+    import synth
+    M, K, G, P = wl.M, wl.K, wl.G, wl.P
+    short = M <= 16
+    C = copies if short else 2
+    pl, tl, cl = synth.rotations(wl)
+    rec = torch.from_numpy(np.stack([pq.build_records(p, t) for p, t in zip(pl, tl)])).to(dev)
+    cs = torch.from_numpy(np.stack(cl)).to(dev)
+    xs = [torch.from_numpy(synth.activations(wl)).to(dev) for _ in range(C)]
+    rs = [torch.from_numpy(synth.residual(wl)).to(dev) for _ in range(C)]
+    w = torch.from_numpy(synth.norm_weight(wl)).to(dev)
+    w1 = (1.0 + w.float())
+    ro = torch.empty((M, K), dtype=torch.float16, device=dev)
+    hs = torch.empty((M, K), dtype=torch.float16, device=dev)
+    A = torch.empty((P, M, K), dtype=torch.uint8, device=dev)
+    S = torch.empty((P, M, G), dtype=torch.float32, device=dev)
+    R = torch.empty((P, M, G), dtype=torch.float32, device=dev)
+    fused = lambda i: pq.add_rms_rotate_quant(xs[i % C], rs[i % C], w, 1e-6, rec, cs, residual_out=ro, out=(hs, A, S, R))
+
+    def chain(i):
+        h = xs[i % C].float().add_(rs[i % C].float()).half()
+        hn = torch.nn.functional.rms_norm(h.float(), (K,), weight=w1, eps=1e-6).half()
+        pq.rotate_quant(hn, rec, cs, out=(A, S, R))
+
+    def timed(fn, reps):
+        for i in range(C):
+            fn(i)
+        torch.cuda.synchronize()
+        if short:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(C):
+                    fn(i)
+            graph.replay()
+            torch.cuda.synchronize()
+            e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in e:
+                a.record()
+                graph.replay()
+                b.record()
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) for a, b in e])) * 1e-3 / C
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (a, b) in enumerate(e):
+            a.record()
+            fn(i)
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in e])) * 1e-3
+
+    t_f = timed(fused, 5 if short else 6)
+    t_c = timed(chain, 5 if short else 6)
+    nbytes = 2 * M * K * 2 + K * 2 + P * K * 2 + P * 8 * (K // 2) * 8 + 2 * M * K * 2 + P * M * K + 2 * P * M * G * 4
+    return {"M": M, "K": K, "partitions": P, "fused_us": round(t_f * 1e6, 2), "chain_us": round(t_c * 1e6, 2),
+            "bytes": nbytes, "fused_GBs": round(nbytes / t_f / 1e9, 1),
+            "chain": "torch add + torch rms_norm (float32) + pq_rotate_quant",
+            "timing": (f"HIP graph of {C} launches over {C} copies, per-launch median of 5 replays" if short
+                       else "HIP events around each eager call, median of 6, two alternating copies")}
 
 
 def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False, w5=False):

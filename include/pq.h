@@ -239,6 +239,28 @@ int pq_gemm5(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, i
              int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream);
 
 /*
+ * Fused producer (device): residual add + RMSNorm + the per-group rotate-quant, one launch.
+ * Source: "2026-09-02/03: rotation stream (fused add + RMSNorm + rotate + quant producers)"
+ * (one kernel per norm-fed linear returning the normalised row, the new residual and A/ASG/RS;
+ * the residual exact, the normalised row within ppm of a CPU reference). Per token row:
+ *   h = fl16(f32(x) + f32(res));                       the new residual, written to res_out
+ *   hs = fl16((h * rstd) * w'),  rstd = 1 / sqrt(mean_k(h^2) + eps),  w' = 1 + w (gemma != 0)
+ *        or w (gemma == 0), all in binary32 (the row's sum of squares in a fixed order)
+ *   A, ASG, RS = pq_rotate_quant of hs (same arithmetic, every partition).
+ *
+ * x_d, res_d  f16 [M, ldx] / [M, ldr] (first K columns used); res_out_d f16 [M, ldo] (may be
+ *             res_d itself: each element is read before it is written); w_d f16 [K].
+ * hs_d        out f16 [M, K] contiguous.
+ * rec_d, cs_d, a_d, asg_d, rs_d  as pq_rotate_quant.
+ * eps > 0 and finite; 1 <= P <= 3; K % 128 == 0 and K <= 18432 (each row is kept on chip);
+ * x_d, res_d, res_out_d, w_d, hs_d 16-byte aligned, ldx, ldr, ldo multiples of 8 and >= K.
+ */
+int pq_add_rms_rotate_quant(const uint16_t* x_d, int64_t ldx, const uint16_t* res_d, int64_t ldr,
+                            const uint16_t* w_d, float eps, int gemma, int M, int K, int P,
+                            const void* rec_d, const uint16_t* cs_d, uint16_t* res_out_d, int64_t ldo,
+                            uint16_t* hs_d, uint8_t* a_d, float* asg_d, float* rs_d, pq_stream_t stream);
+
+/*
  * Verification hooks: run the exact device arithmetic the prologue uses on plain arrays, so
  * tests can check it exhaustively.
  *  pq_e4m3_encode: codes_d[i] = E(q_d[i]) with the prologue's encoder (n >= 0).

@@ -54,6 +54,8 @@ SIGNATURES = {
     "pq_packed_weight5_bytes": (_SZ, [_I, _I]),
     "pq_pack_weights5": (_I, [_P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "pq_gemm5": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
+    "pq_add_rms_rotate_quant": (_I, [_P, _I64, _P, _I64, _P, ctypes.c_float, _I, _I, _I, _I, _P, _P, _P, _I64,
+                                     _P, _P, _P, _P, _P]),
     "pq_e4m3_encode": (_I, [_P, _P, _I64, _P]),
     "pq_recip_f32": (_I, [_P, _P, _I64, _P]),
 }
@@ -250,6 +252,36 @@ def gemm5(A, ASG, RS, wpk5, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, w
         _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk5), _ptr(sz), N, pb1, pb2,
         _ptr(out), out.stride(0), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return out
+
+
+def add_rms_rotate_quant(x, residual, weight, eps, rec, cs, gemma=True, residual_out=None, out=None, stream=None):
+    """Fused producer: x, residual f16 [M, K] (row strides multiples of 8), weight f16 [K], rec
+    [P, 8, K/2, 8], cs f16 [P, K] -> (residual_out f16 [M, K] (``residual`` itself may be passed to
+    update it in place), hs f16 [M, K], A u8 [P, M, K], ASG f32 [P, M, G], RS f32 [P, M, G])."""
+    import torch
+    for t, name in ((x, "x"), (residual, "residual")):
+        if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+            raise TypeError(f"{name}: expected a CUDA float16 [M, K] tensor with unit column stride")
+    _need(weight, torch.float16, "weight")
+    _need(rec, torch.uint8, "rec")
+    _need(cs, torch.float16, "cs")
+    M, K = x.shape
+    P = cs.shape[0] if cs.dim() == 2 else 1
+    G = K // GROUP
+    if residual_out is None:
+        residual_out = torch.empty((M, K), dtype=torch.float16, device=x.device)
+    if out is None:
+        hs = torch.empty((M, K), dtype=torch.float16, device=x.device)
+        A = torch.empty((P, M, K), dtype=torch.uint8, device=x.device)
+        S = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
+        R = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
+    else:
+        hs, A, S, R = out
+    _check("pq_add_rms_rotate_quant", lib().pq_add_rms_rotate_quant(
+        _ptr(x), x.stride(0), _ptr(residual), residual.stride(0), _ptr(weight), float(eps), 1 if gemma else 0,
+        M, K, P, _ptr(rec), _ptr(cs), _ptr(residual_out), residual_out.stride(0), _ptr(hs), _ptr(A), _ptr(S),
+        _ptr(R), _stream(stream)))
+    return residual_out, hs, A, S, R
 
 
 def rotate_quant_i8(x, rec, cs, out=None, stream=None):

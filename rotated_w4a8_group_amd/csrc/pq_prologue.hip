@@ -391,6 +391,169 @@ __global__ __launch_bounds__(64 * kTokWaves) void rotate_quant_tok_kernel(
   }
 }
 
+// Sum over the 16 lanes of a row (every lane gets it), in a fixed order.
+__device__ __forceinline__ float row_sum_f(float v) {
+  v += __builtin_bit_cast(float, dpp<0xB1>(__builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, dpp<0x4E>(__builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, dpp<0x141>(__builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, dpp<0x140>(__builtin_bit_cast(int, v)));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const _Float16 a = static_cast<_Float16>(lo), b = static_cast<_Float16>(hi);   // round to nearest even
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+// ---------------------------------------------------------------------------------------
+// Fused producer: residual add + RMSNorm + the per-group rotate-quant, for all partitions. One
+// 16-wave workgroup per quad of 4 tokens (lane: token t = lane/16, 8 channels 8c..8c+7 of each
+// group, c = lane%16). The norm needs the whole row before any group is normalised, so each wave
+// keeps its groups' residual-added values in registers (packed f16, <= 9 groups per wave, K <=
+// 18432) while the row's sum of squares is reduced over the workgroup; it then writes the
+// normalised row and runs, per partition, the per-group prologue on it: channel scale, the 8
+// rotation layers through the wave's LDS quad image, group amax, e4m3 encode and code-domain
+// row-sums, with the arithmetic of rotate_quant_kernel.
+template <int NPG>
+__global__ __launch_bounds__(64 * kTokWaves) void add_rms_rotate_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* res, int64_t ldr,
+    const uint16_t* __restrict__ nw, float eps, int gemma, int M, int K, int P,
+    const uint2* __restrict__ rec, const uint16_t* __restrict__ cs, uint16_t* res_out, int64_t ldo,
+    uint16_t* __restrict__ hs, uint8_t* __restrict__ A, float* __restrict__ ASG, float* __restrict__ RS) {
+  __shared__ __align__(16) uint8_t qbuf[kTokWaves][kProQuadBytes];
+  __shared__ float tred[kTokWaves][4];
+
+  const int G = K >> 7, half = K >> 1;
+  const int m0 = 4 * blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, t = lane >> 4, c = lane & 15;
+  const int m = m0 + t, mld = min(m, M - 1);      // clamped: always a valid row to read
+  uint8_t* const buf = qbuf[wave];
+  uint8_t* const slot = buf + (9 * c) * 16 + 4 * t;
+
+  // residual add; the new residual is stored as the page's producer returns it (res_out may be
+  // res itself: each element is read before the same lane writes it)
+  uint32_t hp[NPG][4];
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NPG; ++j) {
+    const int g = wave + kTokWaves * j;
+    if (g < G) {
+      const int col = g * 128 + 8 * c;
+      const uint4 xs = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(mld) * ldx + col);
+      const uint4 rs = *reinterpret_cast<const uint4*>(res + static_cast<size_t>(mld) * ldr + col);
+      const uint32_t xw[4] = {xs.x, xs.y, xs.z, xs.w}, rw[4] = {rs.x, rs.y, rs.z, rs.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hp[j][i] = pack_f16x2(half_lo(xw[i]) + half_lo(rw[i]), half_hi(xw[i]) + half_hi(rw[i]));
+        const float a = half_lo(hp[j][i]), b = half_hi(hp[j][i]);
+        ss += a * a;
+        ss += b * b;
+      }
+      if (m < M)
+        *reinterpret_cast<uint4*>(res_out + static_cast<size_t>(m) * ldo + col) = make_uint4(hp[j][0], hp[j][1], hp[j][2], hp[j][3]);
+    }
+  }
+  // mean square over the row: the token's 16 lanes, then the waves in order
+  ss = row_sum_f(ss);
+  if (c == 0) tred[wave][t] = ss;
+  __syncthreads();
+  float tot = tred[0][t];
+#pragma unroll
+  for (int w = 1; w < kTokWaves; ++w) tot += tred[w][t];
+  const float rstd = 1.0f / __builtin_sqrtf(tot / static_cast<float>(K) + eps);
+
+  // normalised row: (h * rstd) * w', rounded once to f16
+#pragma unroll
+  for (int j = 0; j < NPG; ++j) {
+    const int g = wave + kTokWaves * j;
+    if (g < G) {
+      const int col = g * 128 + 8 * c;
+      const uint4 ws = *reinterpret_cast<const uint4*>(nw + col);
+      const uint32_t ww[4] = {ws.x, ws.y, ws.z, ws.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float wl = gemma ? 1.0f + half_lo(ww[i]) : half_lo(ww[i]);
+        const float wh = gemma ? 1.0f + half_hi(ww[i]) : half_hi(ww[i]);
+        hp[j][i] = pack_f16x2((half_lo(hp[j][i]) * rstd) * wl, (half_hi(hp[j][i]) * rstd) * wh);
+      }
+      if (m < M)
+        *reinterpret_cast<uint4*>(hs + static_cast<size_t>(m) * K + col) = make_uint4(hp[j][0], hp[j][1], hp[j][2], hp[j][3]);
+    }
+  }
+
+  // the per-group prologue on the normalised row, for each group and partition
+#pragma unroll
+  for (int j = 0; j < NPG; ++j) {
+    const int g = wave + kTokWaves * j;
+    if (g >= G) continue;
+    for (int p = 0; p < P; ++p) {
+      const uint2* const recp = rec + static_cast<size_t>(p) * PQ_LAYERS * half + lane + g * 64;
+      const size_t row = static_cast<size_t>(p) * M + m;
+      uint2 q[PQ_LAYERS];
+#pragma unroll
+      for (int r = 0; r < PQ_LAYERS; ++r) q[r] = recp[static_cast<size_t>(r) * half];
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(cs + static_cast<size_t>(p) * K + g * 128 + 8 * c);
+      const uint32_t cs4[4] = {cw[0], cw[1], cw[2], cw[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<float*>(slot + (2 * i) * 16) = half_lo(hp[j][i]) * half_lo(cs4[i]);
+        *reinterpret_cast<float*>(slot + (2 * i + 1) * 16) = half_hi(hp[j][i]) * half_hi(cs4[i]);
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < PQ_LAYERS; ++r) {
+        const uint32_t ta = lds_row_bytes(q[r].x & 0x7Fu), ha = lds_row_bytes((q[r].x >> 8) & 0x7Fu);
+        const float cr = f16_to_f32(q[r].y), sr = f16_to_f32(q[r].y >> 16);
+        const float4 a = *reinterpret_cast<const float4*>(buf + ta);
+        const float4 b = *reinterpret_cast<const float4*>(buf + ha);
+        const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+        float na[4], nb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float ca = cr * av[k], sb = sr * bv[k];
+          const float cb = cr * bv[k], sa = sr * av[k];
+          na[k] = ca + sb;
+          nb[k] = cb - sa;
+        }
+        *reinterpret_cast<float4*>(buf + ta) = make_float4(na[0], na[1], na[2], na[3]);
+        *reinterpret_cast<float4*>(buf + ha) = make_float4(nb[0], nb[1], nb[2], nb[3]);
+        __builtin_amdgcn_wave_barrier();
+      }
+      float v[8];
+      float gmax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[i] = *reinterpret_cast<const float*>(slot + i * 16);
+        gmax = __builtin_fmaxf(gmax, __builtin_fabsf(v[i]));
+      }
+      __builtin_amdgcn_wave_barrier();
+      const float amax = row_max(gmax);               // over the token's 16 lanes: the group
+      const float asg = amax * 0x1.24924ap-9f;        // fl32(1/448)
+      const float inv = recip_rn(asg);
+      const bool inv_bad = __builtin_fabsf(inv) == __builtin_inff();
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[i] = v[i] * inv + 0.0f;
+      uint32_t w0 = pack4(sv[0], sv[1], sv[2], sv[3]), w1 = pack4(sv[4], sv[5], sv[6], sv[7]);
+      const uint32_t bad = (nan_bytes(w0) | nan_bytes(w1)) | (inv_bad ? 1u : 0u);
+      if (__builtin_amdgcn_ballot_w64(bad != 0)) {
+        // rare: a NaN or out-of-range value in the wave; the full encoder
+        w0 = e4m3_encode2(v[0] * inv, v[1] * inv) | (e4m3_encode2(v[2] * inv, v[3] * inv) << 16);
+        w1 = e4m3_encode2(v[4] * inv, v[5] * inv) | (e4m3_encode2(v[6] * inv, v[7] * inv) << 16);
+      }
+      const int units = row_sum(code_units(w0, w1));
+      if (m < M) {
+        *reinterpret_cast<uint2*>(A + row * K + g * 128 + 8 * c) = make_uint2(w0, w1);
+        if (c == 0) {
+          ASG[row * G + g] = asg;
+          RS[row * G + g] = static_cast<float>(units) * 0x1p-9f;
+        }
+      }
+    }
+  }
+}
+
 __global__ void e4m3_encode_kernel(const float* __restrict__ q, uint8_t* __restrict__ out, int64_t n) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 2;
   if (i + 1 < n) {
@@ -497,6 +660,46 @@ int pq_rotate_quant_tok(const uint16_t* x_d, int64_t ldx, int M, int K, int P, c
   else PQ_TOK_LAUNCH(9);
 #undef PQ_TOK_LAUNCH
   return launch_status("pq_rotate_quant_tok");
+}
+
+int pq_add_rms_rotate_quant(const uint16_t* x_d, int64_t ldx, const uint16_t* res_d, int64_t ldr,
+                            const uint16_t* w_d, float eps, int gemma, int M, int K, int P,
+                            const void* rec_d, const uint16_t* cs_d, uint16_t* res_out_d, int64_t ldo,
+                            uint16_t* hs_d, uint8_t* a_d, float* asg_d, float* rs_d, pq_stream_t stream) {
+  using namespace pq;
+  clear_error();
+  const char* what = "pq_add_rms_rotate_quant";
+  if (M < 0) return set_error(PQ_ERR_SHAPE, "%s: M=%d < 0", what, M);
+  if (K <= 0 || K % PQ_GROUP || K > kTokWaves * 9 * PQ_GROUP)
+    return set_error(PQ_ERR_SHAPE, "%s: K=%d must be a positive multiple of 128, at most %d", what, K, kTokWaves * 9 * PQ_GROUP);
+  if (P < 1 || P > PQ_MAX_PARTITIONS) return set_error(PQ_ERR_PARTITION, "%s: P=%d must be in 1..3", what, P);
+  if (ldx < K || ldr < K || ldo < K || ldx % 8 || ldr % 8 || ldo % 8)
+    return set_error(PQ_ERR_SHAPE, "%s: row strides must be multiples of 8 and >= K=%d", what, K);
+  if (!(eps > 0.0f) || !(eps < __builtin_inff())) return set_error(PQ_ERR_SHAPE, "%s: eps must be positive and finite", what);
+  if (M == 0) return PQ_OK;
+  if (!x_d || !res_d || !w_d || !rec_d || !cs_d || !res_out_d || !hs_d || !a_d || !asg_d || !rs_d)
+    return set_error(PQ_ERR_NULL, "%s: NULL pointer", what);
+  if (!aligned(x_d, 16) || !aligned(res_d, 16) || !aligned(w_d, 16) || !aligned(res_out_d, 16) || !aligned(hs_d, 16) ||
+      !aligned(rec_d, 8) || !aligned(cs_d, 4) || !aligned(a_d, 16) || !aligned(asg_d, 4) || !aligned(rs_d, 4))
+    return set_error(PQ_ERR_ALIGN, "%s: misaligned pointer", what);
+  const int G = K / PQ_GROUP;
+  const int64_t blocks = (M + 3) / 4;
+  const int npg = (G + kTokWaves - 1) / kTokWaves;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const uint2* rec = static_cast<const uint2*>(rec_d);
+#define PQ_PROD_LAUNCH(NPG)                                                                           \
+  do {                                                                                                \
+    auto kern = add_rms_rotate_quant_kernel<NPG>;                                                     \
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * kTokWaves), 0, s, x_d, ldx, \
+                       res_d, ldr, w_d, eps, gemma ? 1 : 0, M, K, P, rec, cs_d, res_out_d, ldo, hs_d,   \
+                       a_d, asg_d, rs_d);                                                             \
+  } while (0)
+  if (npg <= 1) PQ_PROD_LAUNCH(1);
+  else if (npg <= 3) PQ_PROD_LAUNCH(3);
+  else if (npg <= 5) PQ_PROD_LAUNCH(5);
+  else PQ_PROD_LAUNCH(9);
+#undef PQ_PROD_LAUNCH
+  return launch_status(what);
 }
 
 int pq_e4m3_encode(const float* q_d, uint8_t* codes_d, int64_t n, pq_stream_t stream) {

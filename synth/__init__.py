@@ -32,7 +32,7 @@ NO_BOUNDARY = 2 ** 31 - 1
 AWQ_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
 
 # tensor ids for the seed tuple
-T_X, T_PAIRS, T_THETA, T_CS, T_CODES, T_ZP, T_SCALES, T_OUTCH, T_SMALLG, T_SUBN = range(10)
+T_X, T_PAIRS, T_THETA, T_CS, T_CODES, T_ZP, T_SCALES, T_OUTCH, T_SMALLG, T_SUBN, T_RES, T_NORMW = range(12)
 
 
 @dataclass(frozen=True)
@@ -105,6 +105,17 @@ def activations(wl: Workload, M: Optional[int] = None) -> np.ndarray:
         for g in gs:
             x[:, g * GROUP:(g + 1) * GROUP] *= 1e-3
     return x.astype(np.float16)
+
+
+def residual(wl: Workload, M: Optional[int] = None) -> np.ndarray:
+    """The residual stream beside ``activations``: f16 [M, K] ~ N(0, 2^2)."""
+    M = wl.M if M is None else M
+    return (rng(wl.wid, T_RES).standard_normal((M, wl.K)) * 2.0).astype(np.float16)
+
+
+def norm_weight(wl: Workload) -> np.ndarray:
+    """RMSNorm weights f16 [K] ~ N(0, 0.1^2) (the Gemma form scales by 1 + w)."""
+    return (rng(wl.wid, T_NORMW).standard_normal(wl.K) * 0.1).astype(np.float16)
 
 
 def rotations(wl: Workload):

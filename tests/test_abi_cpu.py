@@ -199,6 +199,24 @@ def test_gemm5_and_pack5_validation():
     assert lib.pq_packed_weight5_bytes(256, 48) == 0
 
 
+def test_add_rms_rotate_quant_validation():
+    f = pq.lib().pq_add_rms_rotate_quant
+    ok = dict(x=FAKE, ldx=256, r=FAKE, ldr=256, w=FAKE, eps=1e-6, gemma=1, M=4, K=256, P=1, rec=FAKE, cs=FAKE,
+              ro=FAKE, ldo=256, hs=FAKE, A=FAKE, S=FAKE, R=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["ldx"], a["r"], a["ldr"], a["w"], a["eps"], a["gemma"], a["M"], a["K"], a["P"], a["rec"],
+                 a["cs"], a["ro"], a["ldo"], a["hs"], a["A"], a["S"], a["R"], None)
+    assert call(M=0) == 0
+    assert call(K=100) == -2 and call(K=18560, ldx=18560, ldr=18560, ldo=18560) == -2
+    assert call(ldx=260) == -2 and call(ldo=128) == -2
+    assert call(eps=0.0) == -2 and call(eps=float("inf")) == -2
+    assert call(P=4) == -4
+    assert call(r=None) == -1 and call(hs=None) == -1
+    assert call(x=ctypes.c_void_p(0x100008)) == -3
+
+
 def _rq(**kw):
     a = dict(x=FAKE, ldx=256, M=4, K=256, P=1, rec=FAKE, cs=FAKE, A=FAKE, asg=FAKE, rs=FAKE, s=None)
     a.update(kw)
