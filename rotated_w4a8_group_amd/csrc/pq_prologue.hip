@@ -413,8 +413,11 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 // 18432) while the row's sum of squares is reduced over the workgroup; it then writes the
 // normalised row and runs, per partition, the per-group prologue on it: channel scale, the 8
 // rotation layers through the wave's LDS quad image, group amax, e4m3 encode and code-domain
-// row-sums, with the arithmetic of rotate_quant_kernel.
-template <int NPG>
+// row-sums, with the arithmetic of rotate_quant_kernel. For few tokens (kChunked) the groups
+// of a quad are cut into chunks of 16, one workgroup each: every workgroup reads the whole row for
+// the sum of squares (the same fixed order, so every chunk gets the same rstd) and keeps, writes
+// and quantises only the group of its chunk that belongs to each wave.
+template <int NPG, bool kChunked>
 __global__ __launch_bounds__(64 * kTokWaves) void add_rms_rotate_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* res, int64_t ldr,
     const uint16_t* __restrict__ nw, float eps, int gemma, int M, int K, int P,
@@ -424,12 +427,15 @@ __global__ __launch_bounds__(64 * kTokWaves) void add_rms_rotate_quant_kernel(
   __shared__ float tred[kTokWaves][4];
 
   const int G = K >> 7, half = K >> 1;
-  const int m0 = 4 * blockIdx.x;
+  const int nchunks = kChunked ? (G + kTokWaves - 1) / kTokWaves : 1;
+  const int m0 = 4 * (blockIdx.x / nchunks), chunk = blockIdx.x % nchunks;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, t = lane >> 4, c = lane & 15;
   const int m = m0 + t, mld = min(m, M - 1);      // clamped: always a valid row to read
   uint8_t* const buf = qbuf[wave];
   uint8_t* const slot = buf + (9 * c) * 16 + 4 * t;
+  // the group j of this wave that this workgroup keeps (all of them unless kChunked)
+  auto mine = [&](int j) { return !kChunked || j == chunk; };
 
   // residual add; the new residual is stored as the page's producer returns it (res_out may be
   // res itself: each element is read before the same lane writes it)
@@ -450,7 +456,7 @@ __global__ __launch_bounds__(64 * kTokWaves) void add_rms_rotate_quant_kernel(
         ss += a * a;
         ss += b * b;
       }
-      if (m < M)
+      if (m < M && mine(j))
         *reinterpret_cast<uint4*>(res_out + static_cast<size_t>(m) * ldo + col) = make_uint4(hp[j][0], hp[j][1], hp[j][2], hp[j][3]);
     }
   }
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(64 * kTokWaves) void add_rms_rotate_quant_kernel(
 #pragma unroll
   for (int j = 0; j < NPG; ++j) {
     const int g = wave + kTokWaves * j;
-    if (g < G) {
+    if (g < G && mine(j)) {
       const int col = g * 128 + 8 * c;
       const uint4 ws = *reinterpret_cast<const uint4*>(nw + col);
       const uint32_t ww[4] = {ws.x, ws.y, ws.z, ws.w};
@@ -486,7 +492,7 @@ __global__ __launch_bounds__(64 * kTokWaves) void add_rms_rotate_quant_kernel(
 #pragma unroll
   for (int j = 0; j < NPG; ++j) {
     const int g = wave + kTokWaves * j;
-    if (g >= G) continue;
+    if (g >= G || !mine(j)) continue;
     for (int p = 0; p < P; ++p) {
       const uint2* const recp = rec + static_cast<size_t>(p) * PQ_LAYERS * half + lane + g * 64;
       const size_t row = static_cast<size_t>(p) * M + m;
@@ -683,13 +689,16 @@ int pq_add_rms_rotate_quant(const uint16_t* x_d, int64_t ldx, const uint16_t* re
       !aligned(rec_d, 8) || !aligned(cs_d, 4) || !aligned(a_d, 16) || !aligned(asg_d, 4) || !aligned(rs_d, 4))
     return set_error(PQ_ERR_ALIGN, "%s: misaligned pointer", what);
   const int G = K / PQ_GROUP;
-  const int64_t blocks = (M + 3) / 4;
   const int npg = (G + kTokWaves - 1) / kTokWaves;
+  // few tokens: one workgroup per (quad, chunk of 16 groups), each reading the whole row for its
+  // sum of squares; many tokens: one workgroup per quad (no row read twice)
+  const bool chunked = M <= 64;
+  const int64_t blocks = static_cast<int64_t>((M + 3) / 4) * (chunked ? npg : 1);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint2* rec = static_cast<const uint2*>(rec_d);
 #define PQ_PROD_LAUNCH(NPG)                                                                           \
   do {                                                                                                \
-    auto kern = add_rms_rotate_quant_kernel<NPG>;                                                     \
+    auto kern = chunked ? add_rms_rotate_quant_kernel<NPG, true> : add_rms_rotate_quant_kernel<NPG, false>; \
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * kTokWaves), 0, s, x_d, ldx, \
                        res_d, ldr, w_d, eps, gemma ? 1 : 0, M, K, P, rec, cs_d, res_out_d, ldo, hs_d,   \
                        a_d, asg_d, rs_d);                                                             \
