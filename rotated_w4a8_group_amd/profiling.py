@@ -122,8 +122,10 @@ def counters_table(db, kernels, cus=256, xcds=8, title="", command=""):
         lines.append(f"# {title}\n")
     if command:
         lines.append(f"Command: `{command}`\n")
-    lines.append("| kernel | dispatches | " + " | ".join(names) + " | matrix-core busy |")
-    lines.append("|---|---:|" + "---:|" * len(names) + "---:|")
+    has_busy = "SQ_VALU_MFMA_BUSY_CYCLES" in names and "GRBM_GUI_ACTIVE" in names
+    extra = " matrix-core busy |" if has_busy else ""
+    lines.append("| kernel | dispatches | " + " | ".join(names) + " |" + extra)
+    lines.append("|---|---:|" + "---:|" * (len(names) + has_busy))
     for pat in kernels:
         med = {}
         n = 0
@@ -132,9 +134,11 @@ def counters_table(db, kernels, cus=256, xcds=8, title="", command=""):
             n = len(v)
             med[c] = statistics.median(v)
         busy = ""
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("GRBM_GUI_ACTIVE"):
-            busy = f"{med['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * cus * med['GRBM_GUI_ACTIVE'] / xcds):.3f}"
-        lines.append(f"| `{pat}` | {n} | " + " | ".join(f"{med[c]:.4g}" for c in names) + f" | {busy} |")
+        if has_busy and med["GRBM_GUI_ACTIVE"]:
+            busy = f" {med['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * cus * med['GRBM_GUI_ACTIVE'] / xcds):.3f} |"
+        elif has_busy:
+            busy = "  |"
+        lines.append(f"| `{pat}` | {n} | " + " | ".join(f"{med[c]:.4g}" for c in names) + " |" + busy)
     return "\n".join(lines) + "\n"
 
 
