@@ -58,11 +58,27 @@ def prologue_bytes(M, K, P=1):
     return M * K * 2 + P * K * 2 + P * 8 * (K // 2) * 8 + P * M * K + 2 * P * M * G * 4
 
 
+def settle_clock(torch, fn, n, ms=30.0):
+    """Untimed calls fn(0), fn(1), ... for about `ms` of wall time (synchronising every n calls),
+    so that the timed calls after it run at the GPU's settled clock rather than during its ramp
+    after the host-side set-up of a measurement."""
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        fn(i % n)
+        i += 1
+        if i % n == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 200 steps after 50 warm-up steps (about 60 ms of GPU work): the GPU's clock settles over the
+    # first few ms of a process, and 20 steps after 5 read the GEMM 15% slower than steady state
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--copies", type=int, default=12)
     ap.add_argument("--decode-reps", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -213,6 +229,7 @@ def main():
                     pq.gemm(Ad, Sd, Rd, wq[i][0], wq[i][1], N, out=yd)
             graph.replay()
             torch.cuda.synchronize()
+            settle_clock(torch, lambda i: graph.replay(), 1)
             reps = max(3, args.decode_reps // C)
             e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
             for i in range(reps):
@@ -227,7 +244,7 @@ def main():
                              "us_p90": round(float(np.percentile(t, 90)) * 1e6, 2),
                              "bytes": gemm_bytes(Md, K, N), "GBs": round(float(gbs), 1),
                              "frac_hbm": round(float(gbs) / PEAK_HBM_GBS, 4),
-                             "timing": f"HIP graph of {C} launches over {C} weight copies, per-launch average"}
+                             "timing": f"HIP graph of {C} launches over {C} weight copies, per-launch average after ~30 ms of untimed replays"}
         out["decode"] = dec
 
     # ---- every other configuration: prologue and GEMM timed separately
@@ -317,6 +334,7 @@ def producer_measurement(wl, pq, torch, np, dev, copies):
                     fn(i)
             graph.replay()
             torch.cuda.synchronize()
+            settle_clock(torch, lambda i: graph.replay(), 1)
             e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
             for a, b in e:
                 a.record()
@@ -324,6 +342,7 @@ def producer_measurement(wl, pq, torch, np, dev, copies):
                 b.record()
             torch.cuda.synchronize()
             return float(np.median([a.elapsed_time(b) for a, b in e])) * 1e-3 / C
+        settle_clock(torch, fn, C)
         e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for i, (a, b) in enumerate(e):
             a.record()
@@ -338,8 +357,8 @@ def producer_measurement(wl, pq, torch, np, dev, copies):
     return {"M": M, "K": K, "partitions": P, "fused_us": round(t_f * 1e6, 2), "chain_us": round(t_c * 1e6, 2),
             "bytes": nbytes, "fused_GBs": round(nbytes / t_f / 1e9, 1),
             "chain": "torch add + torch rms_norm (float32) + pq_rotate_quant",
-            "timing": (f"HIP graph of {C} launches over {C} copies, per-launch median of 5 replays" if short
-                       else "HIP events around each eager call, median of 6, two alternating copies")}
+            "timing": (f"HIP graph of {C} launches over {C} copies, per-launch median of 5 replays after ~30 ms of untimed replays" if short
+                       else "HIP events around each eager call, median of 6 after ~30 ms of untimed calls, two alternating copies")}
 
 
 def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False, w5=False):
@@ -397,6 +416,7 @@ def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False, w5=F
                     fn(i)
             graph.replay()
             torch.cuda.synchronize()
+            settle_clock(torch, lambda i: graph.replay(), 1)
             e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
             for a, b in e:
                 a.record()
@@ -404,6 +424,7 @@ def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False, w5=F
                 b.record()
             torch.cuda.synchronize()
             return float(np.median([a.elapsed_time(b) for a, b in e])) * 1e-3 / C
+        settle_clock(torch, fn, C)
         e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for i, (a, b) in enumerate(e):
             a.record()
@@ -423,10 +444,10 @@ def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False, w5=F
            "gemm_bytes": gb, "gemm_GBs": round(gb / t_gem / 1e9, 1)}
     if short:
         res["roofline"] = {"bound": "hbm", "frac": round(gb / t_gem / 1e9 / PEAK_HBM_GBS, 4)}
-        res["timing"] = f"HIP graph of {C} launches over {C} copies, per-launch median of 5 replays"
+        res["timing"] = f"HIP graph of {C} launches over {C} copies, per-launch median of 5 replays after ~30 ms of untimed replays"
     else:
         res["roofline"] = {"bound": "mfma", "frac": round(flops / t_gem / 1e12 / PEAK_FP8_TFLOPS, 4)}
-        res["timing"] = "HIP events around each eager call, median of 6, two alternating copies"
+        res["timing"] = "HIP events around each eager call, median of 6 after ~30 ms of untimed calls, two alternating copies"
     del xs, wq, A, S, R, y, ws
     torch.cuda.empty_cache()
     return res

@@ -80,6 +80,8 @@ def test_end_to_end_full_shapes(name):
 @pytest.mark.parametrize("M,K,N,splits", [
     (17, 256, 144, ()), (130, 384, 272, (128, 144)), (1, 128, 16, ()), (16, 640, 96, ()),
     (33, 256, 384, (128, 128, 128)), (300, 1024, 2048, ()),
+    # whole 256x256 tiles only, with 9, 1 and 3 groups (odd and short group counts)
+    (512, 1152, 512, ()), (256, 128, 256, ()), (256, 384, 512, ()),
 ])
 def test_gemm_ragged_shapes(M, K, N, splits):
     wl = synth.Workload("ragged", 50 + M, M, K, N, splits=splits)

@@ -155,7 +155,7 @@ def test_tok_end_to_end_full_shapes(name):
 
 @pytest.mark.parametrize("M,K,N,splits", [
     (17, 256, 144, ()), (130, 384, 272, (128, 144)), (1, 128, 16, ()), (33, 256, 384, (128, 128, 128)),
-    (300, 1024, 2048, ()),
+    (300, 1024, 2048, ()), (512, 1152, 512, ()),
 ])
 def test_gemm_tok_ragged_shapes(M, K, N, splits):
     wl = synth.Workload("tokragged", 90 + M, M, K, N, splits=splits)
