@@ -837,8 +837,6 @@ struct PrefillMap {
   int full;      // workgroups that run whole tiles (whole rounds); the rest run pieces
   int split;     // pieces per remaining tile: 1, 2, 4 or 8 (wide) / 1 or 2 (narrow) / 1, 2 or 4 (flat)
   int shape;     // PfShape
-  int stag_full; // launch order (0: off): stag_full whole tiles, then stag_pieces pieces, then
-  int stag_pieces;  // the other whole tiles, then the other pieces (both multiples of 8)
 };
 
 template <bool kTok, bool kI8, bool kW5>
@@ -848,16 +846,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
     const u32x4* __restrict__ zpa, const uint32_t* __restrict__ sz, int N, int pb1, int pb2,
     uint16_t* __restrict__ y, int64_t ldy, PrefillMap map, bool vec16) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfLds];
-  int b = blockIdx.x;
-  if (map.stag_full > 0) {
-    // Half of the CUs run their share of the last round's pieces first, so the two halves finish
-    // their whole tiles (and write their outputs) at different times rather than all at once.
-    // Every offset is a multiple of 8, so a workgroup keeps the XCD (blockIdx % 8) that the
-    // tile numbering assumes.
-    const int h = map.stag_full, s2 = map.stag_pieces;
-    if (b >= h && b < h + s2) b = map.full + (b - h);
-    else if (b >= h + s2 && b < map.full + s2) b -= s2;
-  }
+  const int b = blockIdx.x;
   const int bm = map.shape == kPfWide ? 256 : 128, bn = map.shape == kPfNarrow ? 128 : 256;
   const bool piece = b >= map.full;
   const int big = piece ? map.full + (b - map.full) / map.split : b;
@@ -914,11 +903,6 @@ PrefillMap prefill_map(int M, int N, int shape, int cus) {
     static const int cands[3][3] = {{8, 4, 2}, {2, 0, 0}, {4, 2, 0}};
     for (int i = 0; i < 3 && cands[shape][i]; ++i)
       if (rem * cands[shape][i] <= cus) { m.split = cands[shape][i]; break; }
-    const int64_t pieces = rem * m.split;
-    if (full >= cus && pieces >= 16) {
-      m.stag_full = (cus / 2) / 8 * 8;
-      m.stag_pieces = static_cast<int>(pieces / 2) / 8 * 8;
-    }
   }
   return m;
 }
