@@ -249,6 +249,61 @@ def test_pack_validation():
     assert L.pq_packed_weight_bytes(100, 16) == 0
 
 
+def _gemm_variant(name, **kw):
+    a = dict(a=FAKE, asg=FAKE, rs=FAKE, M=4, K=256, P=1, wpk=FAKE, sz=FAKE, N=128,
+             pb1=pq.NO_BOUNDARY, pb2=pq.NO_BOUNDARY, y=FAKE, ldy=128, ws=FAKE, ws_bytes=1 << 24, s=None)
+    a.update(kw)
+    return getattr(pq.lib(), name)(a["a"], a["asg"], a["rs"], a["M"], a["K"], a["P"], a["wpk"], a["sz"],
+                                   a["N"], a["pb1"], a["pb2"], a["y"], a["ldy"], a["ws"], a["ws_bytes"], a["s"])
+
+
+@pytest.mark.parametrize("name", ["pq_gemm_tok", "pq_gemm_i8"])
+def test_gemm_variant_validation(name):
+    assert _gemm_variant(name, M=0, a=None, y=None) == 0
+    assert _gemm_variant(name, K=100) == -2 and _gemm_variant(name, N=120) == -2
+    assert _gemm_variant(name, ldy=64) == -2 and _gemm_variant(name, M=-1) == -2
+    assert _gemm_variant(name, P=2) == -4 and _gemm_variant(name, P=4) == -4
+    assert _gemm_variant(name, a=None) == -1 and _gemm_variant(name, rs=None) == -1
+    assert _gemm_variant(name, y=ctypes.c_void_p(0x100002)) == -3
+    assert _gemm_variant(name, M=32, ws=None, ws_bytes=1 << 20) == -1
+    assert pq.lib().pq_last_error().decode().startswith(name)
+
+
+def test_gemm_tok_workspace_sizes():
+    L = pq.lib()
+    # decode (M <= 16): the token scale repeated for every group, 3 partitions, 256-byte multiple
+    assert L.pq_gemm_tok_workspace_bytes(8, 17408, 5120) == (3 * 8 * 40 * 4 + 255) // 256 * 256
+    # prefill: the zero-point activation operand only (no transposed group scales)
+    assert L.pq_gemm_tok_workspace_bytes(2048, 17408, 5120) == 3 * 128 * 4 * 1024
+    assert L.pq_gemm_tok_workspace_bytes(0, 17408, 5120) == 0
+    assert L.pq_gemm_tok_workspace_bytes(8, 17408, 100) == 0
+
+
+def _rq_variant(name, **kw):
+    a = dict(x=FAKE, ldx=256, M=4, K=256, P=1, rec=FAKE, cs=FAKE, A=FAKE, asg=FAKE, rs=FAKE, s=None)
+    a.update(kw)
+    return getattr(pq.lib(), name)(a["x"], a["ldx"], a["M"], a["K"], a["P"], a["rec"], a["cs"],
+                                   a["A"], a["asg"], a["rs"], a["s"])
+
+
+@pytest.mark.parametrize("name", ["pq_rotate_quant_tok", "pq_rotate_quant_i8"])
+def test_prologue_variant_validation(name):
+    assert _rq_variant(name, M=0, x=None, A=None) == 0
+    assert _rq_variant(name, K=200) == -2 and _rq_variant(name, M=-2) == -2
+    assert _rq_variant(name, ldx=128) == -2
+    assert _rq_variant(name, P=0) == -4 and _rq_variant(name, P=4) == -4
+    assert _rq_variant(name, x=None) == -1 and _rq_variant(name, rs=None) == -1
+    assert _rq_variant(name, x=ctypes.c_void_p(0x100002)) == -3
+    assert pq.lib().pq_last_error().decode().startswith(name)
+
+
+def test_prologue_tok_row_limit():
+    # the per-token kernel keeps a whole row on chip: at most 16 waves x 9 groups x 128 channels
+    assert _rq_variant("pq_rotate_quant_tok", K=18432, ldx=18432, M=0) == 0
+    assert _rq_variant("pq_rotate_quant_tok", K=18560, ldx=18560) == -2
+    assert _rq_variant("pq_rotate_quant_tok", ldx=257) == -2   # odd row stride
+
+
 def test_hooks_validation():
     L = pq.lib()
     assert L.pq_e4m3_encode(FAKE, FAKE, -1, None) == -2
