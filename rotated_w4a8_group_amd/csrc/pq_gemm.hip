@@ -549,7 +549,7 @@ constexpr int kPfStages = 3;
 constexpr int kPfWaves = 8;
 constexpr int kPfLds = kPfStages * 51200;   // the 256x256 ring (the largest)
 
-template <int TM, int TN, int WM, int WN, bool kTok = false, bool kW5 = false>
+template <int TM, int TN, int WM, int WN, bool kTok = false, bool kW5 = false, int S = kPfStages>
 struct PfTile {
   static constexpr int MF = TM / WM / 16, NF = TN / WN / 16;   // fragments per wave
   static constexpr int kOffA = 0;                              // [TM rows][8 chunks][16 B], chunks swizzled
@@ -564,7 +564,7 @@ struct PfTile {
   static constexpr int kPerWave = (nD + 3) / 4;                 // loads per wave of the issuing half
   static constexpr int kOutStride = TN + 8;                    // bf16 per staged output row
   static_assert(WM * WN == kPfWaves && MF >= 1 && NF >= 1 && TM % 64 == 0 && TN % 64 == 0, "tile");
-  static_assert(kPfStages * kStage <= kPfLds && TM * kOutStride * 2 <= kPfLds, "LDS");
+  static_assert(S >= 2 && S * kStage <= kPfLds && TM * kOutStride * 2 <= kPfLds, "LDS");
   static_assert(kPerWave <= 31, "vmcnt");
 };
 
@@ -608,13 +608,15 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
   return bid < 8 * q ? (bid % 8) * q + bid / 8 : bid;
 }
 
-template <int TM, int TN, int WM, int WN, bool kTok, bool kI8, bool kW5>
+template <int TM, int TN, int WM, int WN, bool kTok, bool kI8, bool kW5, int S = kPfStages>
 __device__ __forceinline__ void prefill_tile(
     const uint8_t* __restrict__ A, const float* __restrict__ ASGT, int M, int K,
     const u32x4* __restrict__ wpk, const uint32_t* __restrict__ hi, const u32x4* __restrict__ zpe,
     const u32x4* __restrict__ zpa, const uint32_t* __restrict__ sz, int N, int p, int m0, int n0,
     uint16_t* __restrict__ y, int64_t ldy, bool vec16, uint8_t* smem) {
-  using TL = PfTile<TM, TN, WM, WN, kTok, kW5>;
+  using TL = PfTile<TM, TN, WM, WN, kTok, kW5, S>;
+  static_assert(S == 2 || S == 3, "the wait counts below cover rings of 2 and 3 stages");
+  constexpr int D = S - 1;   // groups loaded ahead
   constexpr int MF = TL::MF, NF = TL::NF, PW = TL::kPerWave;
   const int G = K >> 7;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -687,18 +689,21 @@ __device__ __forceinline__ void prefill_tile(
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // Group j's loads go into stage j % S and are issued during group j - D (D = S - 1 groups
+  // ahead; the first D groups before the loop) by half (j - D) % 2.
   const int half = wave >> 2;
-  if (half == 0) issue(0, 0);
-  if (G > 1 && half == 1) issue(1, 1);
+  for (int j = 0; j < D && j < G; ++j)
+    if (((j - D) & 1) == half) issue(j % S, j);
   for (int g = 0; g < G; ++g) {
-    // Group g was loaded by half g%2, whose only outstanding loads are group g's: it waits for
-    // all of them. The other half's outstanding loads (at most PW, group g+1) need not land. The
-    // barrier then makes group g visible to every wave and guarantees that no wave still reads
-    // stage (g+2)%3. (__syncthreads would also drain the group g+1 loads.)
-    if ((g & 1) == half) wait_vm_lgkm_barrier<0>();
-    else wait_vm_lgkm_barrier<PW>();
-    if (g + 2 < G && (g & 1) == half) issue((g + 2) % kPfStages, g + 2);
-    const uint8_t* st = smem + (g % kPfStages) * TL::kStage;
+    // Group g was loaded by half (g - D) % 2, whose only outstanding loads are group g's: it
+    // waits for all of them. With D = 2 the other half's outstanding loads (at most PW, group
+    // g+1) need not land; with D = 1 it has none. The barrier then makes group g visible to every
+    // wave and guarantees that no wave still reads stage (g + D) % S, the one group g - 1 used.
+    // (__syncthreads would also drain the group g+1 loads.)
+    if (((g - D) & 1) == half) wait_vm_lgkm_barrier<0>();
+    else wait_vm_lgkm_barrier<D >= 2 ? PW : 0>();
+    if (g + D < G && (g & 1) == half) issue((g + D) % S, g + D);
+    const uint8_t* st = smem + (g % S) * TL::kStage;
 
     v8i bf[NF];
     float s9[NF];
@@ -827,15 +832,15 @@ __device__ __forceinline__ void prefill_tile(
   store_tile_rows<TM, TN, TL::kOutStride>(ot, y, ldy, m0, n0, M, N, vec16);
 }
 
-// Tile shapes of the prefill grid: 256x256 (pieces 128x256, 128x128, 64x128), 128x128 (pieces
-// 64x128) when a partition boundary is not on a 256-column line, and 128x256 for int5 weights
-// (pieces 128x128, 64x128), whose fifth-bit planes do not fit three 256x256 stages in LDS.
-enum PfShape : int { kPfWide = 0, kPfNarrow = 1, kPfFlat = 2 };
+// Tile shapes of the prefill grid: 256x256 (pieces 128x256, 128x128, 64x128), or 128x128 (pieces
+// 64x128) when a partition boundary is not on a 256-column line. int5 whole 256x256 tiles run a
+// ring of two stages: the fifth-bit planes make a stage 54 KiB, and three do not fit in LDS.
+enum PfShape : int { kPfWide = 0, kPfNarrow = 1 };
 struct PrefillMap {
   int tiles_m;   // whole tiles per tile column
   int ntiles;    // whole tiles
   int full;      // workgroups that run whole tiles (whole rounds); the rest run pieces
-  int split;     // pieces per remaining tile: 1, 2, 4 or 8 (wide) / 1 or 2 (narrow) / 1, 2 or 4 (flat)
+  int split;     // pieces per remaining tile: 1, 2, 4 or 8 (wide) / 1 or 2 (narrow)
   int shape;     // PfShape
 };
 
@@ -854,25 +859,23 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
   const int t = xcd_tile(big, map.ntiles);
   int m0 = (t % map.tiles_m) * bm, n0 = (t / map.tiles_m) * bn;
   const int split = piece ? map.split : 1;
-  if (map.shape == kPfFlat) {
-    // piece r of a 128x256 tile: split 2 -> 2 column halves; 4 -> 2 row x 2 column
-    if (split == 2) n0 += 128 * r;
-    else if (split == 4) { m0 += 64 * (r & 1); n0 += 128 * (r >> 1); }
-  } else {
-    // piece r of a whole tile: split 2 -> 2 row halves; 4 -> 2 x 2 quarters; 8 -> 4 row x 2 column
-    if (split == 2) m0 += (bm / 2) * r;
-    else if (split == 4) { m0 += 128 * (r & 1); n0 += 128 * (r >> 1); }
-    else if (split == 8) { m0 += 64 * (r & 3); n0 += 128 * (r >> 2); }
-  }
+  // piece r of a whole tile: split 2 -> 2 row halves; 4 -> 2 x 2 quarters; 8 -> 4 row x 2 column
+  if (split == 2) m0 += (bm / 2) * r;
+  else if (split == 4) { m0 += 128 * (r & 1); n0 += 128 * (r >> 1); }
+  else if (split == 8) { m0 += 64 * (r & 3); n0 += 128 * (r >> 2); }
   if (m0 >= M || n0 >= N) return;   // a piece wholly past the matrix
   const int p = (n0 >= pb1) + (n0 >= pb2);
   if constexpr (kW5) {
-    if (map.shape == kPfFlat && split == 1)
-      prefill_tile<128, 256, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else if (map.shape == kPfFlat ? split == 2 : split == 1)
-      prefill_tile<128, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else
-      prefill_tile<64, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (map.shape == kPfWide) {
+      // the fifth-bit planes make a 256x256 stage 54 KiB: a ring of two (one group loaded ahead)
+      if (split == 1) prefill_tile<256, 256, 2, 4, kTok, kI8, true, 2>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+      else if (split == 2) prefill_tile<128, 256, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+      else if (split == 4) prefill_tile<128, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+      else prefill_tile<64, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+      return;
+    }
+    if (split == 1) prefill_tile<128, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
     return;
   }
   if (map.shape == kPfWide) {
@@ -900,7 +903,7 @@ PrefillMap prefill_map(int M, int N, int shape, int cus) {
   m.full = static_cast<int>(full);
   m.split = 1;
   if (rem > 0) {
-    static const int cands[3][3] = {{8, 4, 2}, {2, 0, 0}, {4, 2, 0}};
+    static const int cands[2][3] = {{8, 4, 2}, {2, 0, 0}};
     for (int i = 0; i < 3 && cands[shape][i]; ++i)
       if (rem * cands[shape][i] <= cus) { m.split = cands[shape][i]; break; }
   }
@@ -1050,10 +1053,10 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
                        a_d, asg, rs_d, M, K, wpk, hi, sz, N, map, y_d, ldy);
     return launch_status(what);
   }
-  // 256x256 tiles (one workgroup per CU; 128x256 for int5) unless a partition boundary is not on
+  // 256x256 tiles (one workgroup per CU) unless a partition boundary is not on
   // a 256-column line
   const bool on256 = (pb1 >= N || pb1 % 256 == 0) && (pb2 >= N || pb2 % 256 == 0);
-  const int shape = !on256 ? kPfNarrow : (kW5 ? kPfFlat : kPfWide);
+  const int shape = !on256 ? kPfNarrow : kPfWide;
   const int64_t tiles = static_cast<int64_t>((M + 127) / 128) * ((N + 127) / 128);
   if (tiles * 8 > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "%s: problem too large", what);
   // the prefill kernel addresses a partition's activations with 32-bit lane offsets
