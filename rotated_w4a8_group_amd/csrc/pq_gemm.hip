@@ -530,7 +530,8 @@ int decode_map(int N, int pb1, int pb2, int cus, int maxnt, DecodeMap* map) {
 // ---------------------------------------------------------------------------------------
 // prefill (M > 16). One 512-thread workgroup (8 waves) per output tile of TM x TN; the waves
 // form a WM x WN grid of (TM/WM) x (TN/WN) blocks; one 128-group per k-step. Operands move
-// global -> LDS by direct LDS loads through a 3-stage ring (2 groups ahead). The activation slab
+// global -> LDS by direct LDS loads through a ring of S stages (S - 1 groups ahead: 3 stages, or 2
+// for int5 256x256 tiles whose stage does not fit three times in LDS). The activation slab
 // arrives as whole 128-byte rows (8 rows per load, fully used cache lines) with the 16-byte chunk
 // index XOR-swizzled by (row%8) ^ ((row/8)%2): each 16-lane quarter of a fragment read then
 // covers the 64 LDS banks once (measured on gfx950: (row/2)%8 and row%8 read ~40% slower); the
@@ -876,18 +877,14 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
     }
     if (split == 1) prefill_tile<128, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
     else prefill_tile<64, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    return;
-  }
-  if (map.shape == kPfWide) {
-    if constexpr (!kW5) {
-      if (split == 1) prefill_tile<256, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-      else if (split == 2) prefill_tile<128, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-      else if (split == 4) prefill_tile<128, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-      else prefill_tile<64, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    }
+  } else if (map.shape == kPfWide) {
+    if (split == 1) prefill_tile<256, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 2) prefill_tile<128, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 4) prefill_tile<128, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
   } else {
-    if (split == 1) prefill_tile<128, 128, 2, 4, kTok, kI8, kW5>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4, kTok, kI8, kW5>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (split == 1) prefill_tile<128, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
   }
 }
 
