@@ -75,6 +75,8 @@ def test_gemm5_parity(name):
 @pytest.mark.parametrize("M,K,N,splits", [
     (17, 256, 160, ()), (130, 384, 288, (128, 160)), (1, 128, 32, ()), (16, 640, 96, ()),
     (33, 256, 384, (128, 128, 128)), (300, 1024, 2048, ()), (5, 384, 16 * 515 * 2, ()),
+    # whole 256x256 tiles on the two-stage ring, with 9, 1 and 3 groups
+    (512, 1152, 512, ()), (256, 128, 256, ()), (256, 384, 512, ()),
 ])
 def test_gemm5_ragged_shapes(M, K, N, splits):
     wl = synth.Workload("ragged5", 160 + M, M, K, N, splits=splits)
