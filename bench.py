@@ -58,6 +58,18 @@ def prologue_bytes(M, K, P=1):
     return M * K * 2 + P * K * 2 + P * 8 * (K // 2) * 8 + P * M * K + 2 * P * M * G * 4
 
 
+# timed repetitions of the per-configuration measurements: eager calls (M > 16), and replays of a
+# HIP graph of one launch per weight copy (M <= 16, 12 copies: 120 launches)
+REPS_LONG = 50
+REPS_SHORT = 10
+
+
+def spread(ts):
+    """(median, p10, p90) of a list of seconds."""
+    import numpy as np
+    return float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
+
+
 def settle_clock(torch, fn, n, ms=30.0):
     """Untimed calls fn(0), fn(1), ... for about `ms` of wall time (synchronising every n calls),
     so that the timed calls after it run at the GPU's settled clock rather than during its ramp
@@ -160,7 +172,8 @@ def main():
     t1 = time.perf_counter()
     ms_per_step_eager = (t1 - t0) * 1e3 / args.steps
     pro_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    gemm_all = [e[1].elapsed_time(e[2]) for e in evs]
+    gemm_ms = float(np.mean(gemm_all))
     # the timed steps: the K steps (cycling the weight copies) captured once in a HIP graph and
     # replayed, which removes the host launch gaps between the step's kernels
     graph = torch.cuda.CUDAGraph()
@@ -203,6 +216,7 @@ def main():
         "config": {"workload": "gate_up prefill: rotate-quant prologue + W4A8 GEMM",
                    "M": M, "K": K, "N": N, "partitions": P, "dram_fed_copies": C},
         "gemm_us": round(gemm_ms * 1e3, 2),
+        "gemm_us_p10_p90": [round(float(np.percentile(gemm_all, q)) * 1e3, 2) for q in (10, 90)],
         "prologue_us": round(pro_ms * 1e3, 2),
         "gemm_tflops": round(gemm_tflops, 2),
         "gemm_vs_pages_gfx1201": round(gemm_tflops / PAGES_GEMM_TFLOPS, 3),
@@ -251,10 +265,10 @@ def main():
     if not args.no_configs:
         out["configs"] = {"c3_gate_up_m2048": {
             "prologue_us": out["prologue_us"], "prologue_GBs": out["prologue_gbs"],
-            "gemm_us": out["gemm_us"], "gemm_TFLOPs": out["gemm_tflops"],
+            "gemm_us": out["gemm_us"], "gemm_us_p10_p90": out["gemm_us_p10_p90"], "gemm_TFLOPs": out["gemm_tflops"],
             "gemm_GBs": round(gemm_bytes(M, K, N) / (gemm_ms * 1e-3) / 1e9, 1),
             "roofline": {"bound": "mfma", "frac": out["roofline"]["frac"]},
-            "timing": "HIP events around each call, eager, DRAM-fed"}}
+            "timing": f"HIP events around each call of the {args.steps} eager steps (mean), DRAM-fed over {C} copies"}}
         for name, key in (("c2_qkv_m4_p3", "qkv"), ("c4_gate_up_m8192", "full_gate_up"),
                           ("c4_down_m8192", "full_down")):
             out["configs"][name] = config_measurement(synth.WORKLOADS[key], pq, torch, np, dev, C)
@@ -341,7 +355,7 @@ def producer_measurement(wl, pq, torch, np, dev, copies):
                 graph.replay()
                 b.record()
             torch.cuda.synchronize()
-            return float(np.median([a.elapsed_time(b) for a, b in e])) * 1e-3 / C
+            return spread([a.elapsed_time(b) * 1e-3 / C for a, b in e])
         settle_clock(torch, fn, C)
         e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for i, (a, b) in enumerate(e):
@@ -349,16 +363,18 @@ def producer_measurement(wl, pq, torch, np, dev, copies):
             fn(i)
             b.record()
         torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) for a, b in e])) * 1e-3
+        return spread([a.elapsed_time(b) * 1e-3 for a, b in e])
 
-    t_f = timed(fused, 5 if short else 6)
-    t_c = timed(chain, 5 if short else 6)
+    reps = REPS_SHORT if short else REPS_LONG
+    t_f, f10, f90 = timed(fused, reps)
+    t_c, _, _ = timed(chain, reps)
     nbytes = 2 * M * K * 2 + K * 2 + P * K * 2 + P * 8 * (K // 2) * 8 + 2 * M * K * 2 + P * M * K + 2 * P * M * G * 4
-    return {"M": M, "K": K, "partitions": P, "fused_us": round(t_f * 1e6, 2), "chain_us": round(t_c * 1e6, 2),
+    return {"M": M, "K": K, "partitions": P, "fused_us": round(t_f * 1e6, 2),
+            "fused_us_p10_p90": [round(f10 * 1e6, 2), round(f90 * 1e6, 2)], "chain_us": round(t_c * 1e6, 2),
             "bytes": nbytes, "fused_GBs": round(nbytes / t_f / 1e9, 1),
             "chain": "torch add + torch rms_norm (float32) + pq_rotate_quant",
-            "timing": (f"HIP graph of {C} launches over {C} copies, per-launch median of 5 replays after ~30 ms of untimed replays" if short
-                       else "HIP events around each eager call, median of 6 after ~30 ms of untimed calls, two alternating copies")}
+            "timing": (f"HIP graph of {C} launches over {C} copies, per-launch median (p10, p90) of {REPS_SHORT} replays after ~30 ms of untimed replays" if short
+                       else f"HIP events around each eager call, median (p10, p90) of {REPS_LONG} after ~30 ms of untimed calls, two alternating copies")}
 
 
 def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False, w5=False):
@@ -423,7 +439,7 @@ def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False, w5=F
                 graph.replay()
                 b.record()
             torch.cuda.synchronize()
-            return float(np.median([a.elapsed_time(b) for a, b in e])) * 1e-3 / C
+            return spread([a.elapsed_time(b) * 1e-3 / C for a, b in e])
         settle_clock(torch, fn, C)
         e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for i, (a, b) in enumerate(e):
@@ -431,23 +447,23 @@ def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False, w5=F
             fn(i)
             b.record()
         torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) for a, b in e])) * 1e-3
+        return spread([a.elapsed_time(b) * 1e-3 for a, b in e])
 
-    t_pro = timed(pro, 5 if short else 6)
-    t_gem = timed(gem, 5 if short else 6)
+    t_pro, p10, p90 = timed(pro, REPS_SHORT if short else REPS_LONG)
+    t_gem, g10, g90 = timed(gem, REPS_SHORT if short else REPS_LONG)
     flops = 2.0 * M * N * K
     gb = gemm_bytes(M, K, N, P, w5=w5)
     res = {"M": M, "K": K, "N": N, "partitions": P,
-           "prologue_us": round(t_pro * 1e6, 2),
+           "prologue_us": round(t_pro * 1e6, 2), "prologue_us_p10_p90": [round(p10 * 1e6, 2), round(p90 * 1e6, 2)],
            "prologue_GBs": round(prologue_bytes(M, K, P) / t_pro / 1e9, 1),
-           "gemm_us": round(t_gem * 1e6, 2), "gemm_TFLOPs": round(flops / t_gem / 1e12, 2),
-           "gemm_bytes": gb, "gemm_GBs": round(gb / t_gem / 1e9, 1)}
+           "gemm_us": round(t_gem * 1e6, 2), "gemm_us_p10_p90": [round(g10 * 1e6, 2), round(g90 * 1e6, 2)],
+           "gemm_TFLOPs": round(flops / t_gem / 1e12, 2), "gemm_bytes": gb, "gemm_GBs": round(gb / t_gem / 1e9, 1)}
     if short:
         res["roofline"] = {"bound": "hbm", "frac": round(gb / t_gem / 1e9 / PEAK_HBM_GBS, 4)}
-        res["timing"] = f"HIP graph of {C} launches over {C} copies, per-launch median of 5 replays after ~30 ms of untimed replays"
+        res["timing"] = f"HIP graph of {C} launches over {C} copies, per-launch median (p10, p90) of {REPS_SHORT} replays after ~30 ms of untimed replays"
     else:
         res["roofline"] = {"bound": "mfma", "frac": round(flops / t_gem / 1e12 / PEAK_FP8_TFLOPS, 4)}
-        res["timing"] = "HIP events around each eager call, median of 6 after ~30 ms of untimed calls, two alternating copies"
+        res["timing"] = f"HIP events around each eager call, median (p10, p90) of {REPS_LONG} after ~30 ms of untimed calls, two alternating copies"
     del xs, wq, A, S, R, y, ws
     torch.cuda.empty_cache()
     return res
@@ -488,8 +504,14 @@ def cpu_baseline(x0, pl, tl, cl, w, wl):
     dt = time.perf_counter() - t0
     flops = 2.0 * len(rows) * wl.N * wl.K
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{len(rows)} of {wl.M} token rows, all {wl.N} columns, prologue + GEMM "
                       f"({dt:.1f} s wall; BLAS threads for the per-group fp64 products)"}, dt
 
