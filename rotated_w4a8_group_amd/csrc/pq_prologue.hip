@@ -34,7 +34,7 @@ constexpr int kProWaves = 4;                 // waves per workgroup (independent
 constexpr int kProQuads = 2;                 // token quads per wave step
 constexpr int kProStep = 4 * kProQuads;      // tokens per wave step
 constexpr int kProQuadBytes = 144 * 16;      // 128 channel rows + 15 pad rows, 16 B each
-constexpr int kProUnits = 8192;              // aim for about this many wave units
+constexpr int kProUnits = 16384;             // aim for about this many wave units
 
 __device__ __forceinline__ uint32_t lds_row_bytes(uint32_t ch) { return (ch + (ch >> 3)) << 4; }
 
