@@ -182,6 +182,13 @@ def test_gemm_m0_is_noop_and_partition_ok():
     assert _gemm(M=32, ws=None, ws_bytes=1 << 20) == -1
 
 
+def test_gemm_rejects_rows_beyond_32_bit_offsets():
+    # the prefill kernel addresses a partition's activations with 32-bit offsets: M * K must stay
+    # below 2^31 (300000 x 8192 = 2.46e9); the call fails before any launch
+    assert _gemm(M=300000, K=8192, N=128, ws_bytes=1 << 40) == -2
+    assert "too large" in pq.lib().pq_last_error().decode()
+
+
 def test_gemm5_and_pack5_validation():
     lib = pq.lib()
     # int5 needs N % 32 == 0 (the fifth-bit planes hold 32 columns per word)
