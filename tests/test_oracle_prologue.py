@@ -6,6 +6,9 @@
   with torch's float8_e4m3fn conversion.
 * R2: orthogonality (norm preservation, exact inverse) of the fp64 rotation.
 * R3: the inference identity y = rot(x*cs) W^T == x (cs * rot^-1(W))^T.
+* R5: the float32 rotation every parity test uses tracks the fp64 rotation with the same f16
+  records (the one R2/R3 pin) within a derived binary32 bound, and keeps each group's norm inside
+  the interval the f16 coefficients allow.
 * I1-I3: scale, saturation and row-sum invariants on every output group.
 * record building: hand-checked cos/sin rounding and permutation validation.
 """
@@ -147,6 +150,64 @@ def test_R2_orthogonality():
     y16 = records.rotate_f64(v, pairs, theta, exact_angles=False)
     drift = np.abs(np.linalg.norm(y16, axis=1) / np.linalg.norm(v, axis=1) - 1)
     assert drift.max() < 8 * 2.0 ** -10
+
+
+@pytest.mark.parametrize("name", ["tiny", "qkv"])
+def test_R5_f32_rotation_tracks_f64(name):
+    """rotate_f32 (binary32, one rounding per written operation) against rotate_f64 with the same
+    f16 cos/sin (exact_angles=False), per partition, token and 128-group.
+
+    Bound: a layer maps a pair (a, b) to (c a + s b, c b - s a); with one rounding per product and
+    per sum each output is off by at most 2u(|c a| + |s b|) <= 2u (1 + 2^-10) ||(a, b)||, so one
+    layer adds at most 2.85u ||v_g|| to the group's error vector (u = 2^-24), and the later layers
+    scale it by at most (1 + 2^-10) each: ||v32 - v64||_g <= 8 * 2.85 * 1.008 u ||v||_g < 24u ||v||_g.
+    A sign or index slip in either function moves some group by O(||v||_g).
+
+    Norms: one exact layer multiplies ||(a, b)||^2 by c^2 + s^2 of its f16 record, so
+    ||R v||_g / ||v||_g lies between the products over the layers of sqrt(min) and sqrt(max) of
+    c^2 + s^2 over the group's 64 pairs; the binary32 path stays within 24u of that interval."""
+    wl = synth.WORKLOADS[name]
+    x = synth.activations(wl)
+    pl, tl, cl = synth.rotations(wl)
+    u = 2.0 ** -24
+    for pairs, theta, cs in zip(pl, tl, cl):
+        rec = records.build(pairs, theta)
+        v32 = prologue.rotate_f32(x, rec, cs).astype(np.float64)
+        v = x.astype(np.float64) * cs.astype(np.float64)              # x * cs, exact
+        v64 = records.rotate_f64(v, pairs, theta, exact_angles=False, rec=rec)
+        M, K = v.shape
+        G = K // 128
+        n_in = np.linalg.norm(v.reshape(M, G, 128), axis=2)
+        err = np.linalg.norm((v32 - v64).reshape(M, G, 128), axis=2)
+        assert np.all(err <= 24 * u * n_in), (err / np.maximum(n_in, 1e-300)).max() / u
+        kappa = (rec["cos"].astype(np.float64) ** 2 + rec["sin"].astype(np.float64) ** 2).reshape(8, G, 64)
+        lo = np.sqrt(kappa.min(axis=2)).prod(axis=0)                   # [G]
+        hi = np.sqrt(kappa.max(axis=2)).prod(axis=0)
+        ratio = np.linalg.norm(v32.reshape(M, G, 128), axis=2) / n_in
+        assert np.all(ratio >= lo[None, :] - 24 * u) and np.all(ratio <= hi[None, :] + 24 * u)
+        # the interval is narrow: f16 cos/sin keep c^2 + s^2 within a few 2^-11 of 1
+        assert np.all(hi - lo < 8 * 2.0 ** -10)
+
+
+def test_R5_planted_sign_slip_is_caught():
+    """A second-update sign slip (c b + s a) keeps the f32 and f64 paths far apart and breaks the
+    norm interval: the bounds above are not vacuous."""
+    x, pairs, theta, cs = _tiny_inputs(seed=3, K=256, M=4)
+    rec = records.build(pairs, theta)
+    v = x.astype(np.float64) * cs.astype(np.float64)
+    v64 = records.rotate_f64(v, pairs, theta, exact_angles=False, rec=rec)
+    w = (x.astype(np.float32) * cs.astype(np.float32)).astype(np.float32)
+    base = (np.arange(128) // 64) * 128
+    for r in range(8):
+        I, J = rec["i"][r] + base, rec["j"][r] + base
+        a, b = w[:, I].copy(), w[:, J].copy()
+        w[:, I] = rec["cos"][r] * a + rec["sin"][r] * b
+        w[:, J] = rec["cos"][r] * b + rec["sin"][r] * a               # the slip
+    err = np.linalg.norm((w - v64).reshape(4, 2, 128), axis=2)
+    n_in = np.linalg.norm(v.reshape(4, 2, 128), axis=2)
+    assert np.all(err > 1e3 * 24 * 2.0 ** -24 * n_in)
+    ratio = np.linalg.norm(w.astype(np.float64).reshape(4, 2, 128), axis=2) / n_in
+    assert np.abs(ratio - 1).max() > 1e-2
 
 
 def test_R2_single_pair_closed_form():
