@@ -107,6 +107,26 @@ def activations(wl: Workload, M: Optional[int] = None) -> np.ndarray:
     return x.astype(np.float16)
 
 
+def activations_one_signed(wl: Workload, M: Optional[int] = None) -> np.ndarray:
+    """x f16 [M, K] = |N(0, 1)| with round(1% K) seeded outlier channels x20: every value >= 0,
+    as post-activation inputs of a down projection are. With identity rotations
+    (``rotations_identity``) the e4m3 codes stay one-signed, the case where the code-domain
+    zero-point correction cancels hardest against the raw-code products."""
+    M = wl.M if M is None else M
+    x = np.abs(rng(wl.wid, T_X, 1).standard_normal((M, wl.K)))
+    n_out = int(round(0.01 * wl.K))
+    ch = rng(wl.wid, T_OUTCH, 1).choice(wl.K, size=n_out, replace=False)
+    x[:, ch] *= 20.0
+    return x.astype(np.float16)
+
+
+def rotations_identity(wl: Workload):
+    """Per partition: seeded pairs as in ``rotations`` with every angle 0 (cos 1, sin 0: no
+    rotation) and channel scales as in ``rotations``."""
+    pairs_l, theta_l, cs_l = rotations(wl)
+    return pairs_l, [np.zeros_like(t) for t in theta_l], cs_l
+
+
 def residual(wl: Workload, M: Optional[int] = None) -> np.ndarray:
     """The residual stream beside ``activations``: f16 [M, K] ~ N(0, 2^2)."""
     M = wl.M if M is None else M

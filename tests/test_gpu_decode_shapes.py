@@ -2,8 +2,9 @@
 over the workgroups (runs of different lengths), three partitions with uneven widths, one group per
 tile, M = 16, and the down projection's shape (few tiles, long K).
 
-Gates: the oracle's fp64 reference within 2e-3 (relative Frobenius, as every GEMM test); the same
-call repeated and replayed from a captured graph gives the same bits.
+Gates: the oracle's fp64 reference through tests/parity.py (Frobenius 2e-3 and the element-wise
+bound, as every GEMM test); the same call repeated and replayed from a captured graph gives the
+same bits.
 """
 import numpy as np
 import pytest
@@ -14,11 +15,10 @@ import synth
 from oracle import gemm as ogemm
 from oracle import prologue as opro
 
+import parity
 from gpu_util import bf16_to_f64, packed_weights, to_dev
 
 pytestmark = pytest.mark.gpu
-
-TOL = 2e-3
 
 # (M, K, N, partition widths); N/16 tiles against 512 resident workgroups on 256 CUs
 SHAPES = [
@@ -51,9 +51,8 @@ def test_decode_shape_parity_and_determinism(M, K, N, splits):
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     y_ref = ogemm.gemm_ref(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds)
-    rel = ogemm.rel_frobenius(bf16_to_f64(y1), y_ref)
-    print(f"[decode shape] rel={rel:.3e}", flush=True)
-    assert rel <= TOL
+    mags = parity.magnitudes_int4(A, S, w, *wl.bounds)
+    parity.check(f"decode shape M={M} K={K} N={N}", bf16_to_f64(y1), y_ref, mags, wl.bounds, wl.G)
 
 
 def test_decode_graph_replay():

@@ -1,9 +1,11 @@
 """GPU parity of the W4A8 group GEMM against the oracle's same-codes fp64 reference.
 
-Gate: ||y - y_ref||_F / ||y_ref||_F <= 2e-3 overall and per partition (the bf16 output
-rounding floor is ~1.6e-3), rows past M never written (sentinel-checked), at every workload's
-full shape. Workloads up to 2048 rows compare all rows on oracle-made activation codes; the
-8192-row workloads run prologue + GEMM on the GPU and compare sampled rows end to end.
+Gates (tests/parity.py): ||y - y_ref||_F / ||y_ref||_F <= 2e-3 overall and per partition, every
+element within the derived bound, rows past M never written (sentinel-checked), at every
+workload's full shape. Workloads up to 2048 rows compare all rows on oracle-made activation codes;
+the 8192-row workloads run prologue + GEMM on the GPU and compare 64 sampled rows end to end.
+One-signed activations (identity rotation, |N(0,1)| with outliers) stress the code-domain
+zero-point correction at decode and prefill sizes.
 """
 import numpy as np
 import pytest
@@ -15,11 +17,11 @@ from oracle import e4m3 as oe4m3
 from oracle import gemm as ogemm
 from oracle import prologue as opro
 
+import parity
 from gpu_util import SENT_BF16, bf16_to_f64, packed_weights, prologue_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-3
 EXTRA_ROWS = 3
 
 
@@ -33,20 +35,16 @@ def _run_gemm(A, S, R, wpk, sz, N, pb1, pb2):
     return ybuf[:M]
 
 
-def _check(name, y, y_ref, wl_bounds, N):
-    rel = ogemm.rel_frobenius(y, y_ref)
-    parts = []
-    pb1, pb2 = wl_bounds
-    edges = [0] + [b for b in (pb1, pb2) if b < N] + [N]
-    for a, b in zip(edges[:-1], edges[1:]):
-        parts.append(ogemm.rel_frobenius(y[:, a:b], y_ref[:, a:b]))
-    print(f"[gemm {name}] rel={rel:.3e} per-partition={[f'{p:.3e}' for p in parts]}", flush=True)
-    assert np.all(np.isfinite(y))
-    assert rel <= TOL and max(parts) <= TOL
+def _check(name, y, A, S, w, wl, rows=None):
+    """Reference and magnitudes for the rows of A/S (all, or `rows`), then every gate."""
+    y_ref = ogemm.gemm_ref(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds, rows=rows)
+    mags = parity.magnitudes_int4(A, S, w, *wl.bounds, rows=rows)
+    parity.check(f"gemm {name}", y, y_ref, mags, wl.bounds, wl.G)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode_m1", "decode_m8", "qkv", "prefill"])
 def test_gemm_parity(name):
+    """All rows, every column (2048 x 17408 at the gate_up prefill workload)."""
     wl = synth.WORKLOADS[name]
     print(f"[gemm {name}] M={wl.M} K={wl.K} N={wl.N} P={wl.P}", flush=True)
     x = synth.activations(wl)
@@ -55,9 +53,25 @@ def test_gemm_parity(name):
     w = synth.weights(wl)
     wpk, sz = packed_weights(w)
     y = _run_gemm(to_dev(A), to_dev(S), to_dev(R), wpk, sz, wl.N, *wl.bounds)
-    rows = np.arange(wl.M) if wl.M <= 64 else np.random.default_rng(5).choice(wl.M, 64, replace=False)
-    y_ref = ogemm.gemm_ref(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds, rows=rows)
-    _check(name, bf16_to_f64(y)[rows], y_ref, wl.bounds, wl.N)
+    _check(name, bf16_to_f64(y), A, S, w, wl)
+
+
+@pytest.mark.parametrize("M", [1, 8, 2048])
+def test_gemm_one_signed_activations(M):
+    """Identity rotations on |N(0,1)| activations with 1% outlier channels x20: every code is
+    non-negative, so the zero-point term (8 sc + zsc) * rs is as large as the raw-code products it
+    cancels against (decode kernel's in-loop form at M <= 16, the prefill kernel's bf16-split
+    epilogue above)."""
+    wl = synth.Workload("onesigned", 95, M, 5120, 17408)
+    print(f"[gemm one-signed] M={M} K={wl.K} N={wl.N}", flush=True)
+    x = synth.activations_one_signed(wl)
+    pl, tl, cl = synth.rotations_identity(wl)
+    A, S, R = opro.rotate_quant(x, pl, tl, cl)
+    assert np.all(A < 0x80)
+    w = synth.weights(wl)
+    wpk, sz = packed_weights(w)
+    y = _run_gemm(to_dev(A), to_dev(S), to_dev(R), wpk, sz, wl.N, *wl.bounds)
+    _check(f"one-signed M={M}", bf16_to_f64(y), A, S, w, wl)
 
 
 @pytest.mark.parametrize("name", ["full_gate_up", "full_down"])
@@ -71,10 +85,9 @@ def test_end_to_end_full_shapes(name):
     w = synth.weights(wl)
     wpk, sz = packed_weights(w)
     y = _run_gemm(A, S, R, wpk, sz, wl.N, *wl.bounds)
-    rows = np.sort(np.concatenate([[0, wl.M - 1], np.random.default_rng(6).choice(np.arange(1, wl.M - 1), 30, replace=False)]))
+    rows = np.sort(np.concatenate([[0, wl.M - 1], np.random.default_rng(6).choice(np.arange(1, wl.M - 1), 62, replace=False)]))
     Ar, Sr, _ = opro.rotate_quant(x[rows], pl, tl, cl)
-    y_ref = ogemm.gemm_ref(Ar, Sr, w.qweight, w.qzeros, w.scales, *wl.bounds)
-    _check(name, bf16_to_f64(y)[rows], y_ref, wl.bounds, wl.N)
+    _check(name, bf16_to_f64(y)[rows], Ar, Sr, w, wl)
 
 
 @pytest.mark.parametrize("M,K,N,splits", [
@@ -91,8 +104,7 @@ def test_gemm_ragged_shapes(M, K, N, splits):
     w = synth.weights(wl)
     wpk, sz = packed_weights(w)
     y = _run_gemm(to_dev(A), to_dev(S), to_dev(R), wpk, sz, N, *wl.bounds)
-    y_ref = ogemm.gemm_ref(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds)
-    _check(f"ragged M={M} K={K} N={N}", bf16_to_f64(y), y_ref, wl.bounds, N)
+    _check(f"ragged M={M} K={K} N={N}", bf16_to_f64(y), A, S, w, wl)
 
 
 @pytest.mark.parametrize("M", [4, 300])
@@ -104,8 +116,7 @@ def test_gemm_subnormal_heavy_codes(M):
     w = synth.weights(wl)
     wpk, sz = packed_weights(w)
     y = _run_gemm(to_dev(A), to_dev(S), to_dev(R), wpk, sz, wl.N, *wl.bounds)
-    y_ref = ogemm.gemm_ref(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds)
-    _check(f"subnormal M={M}", bf16_to_f64(y), y_ref, wl.bounds, wl.N)
+    _check(f"subnormal M={M}", bf16_to_f64(y), A, S, w, wl)
 
 
 @pytest.mark.parametrize("M", [4, 200])

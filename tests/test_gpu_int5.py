@@ -1,10 +1,11 @@
 """GPU parity of the int5 bit-plane weight GEMM (pq_pack_weights5 + pq_gemm5) against
 oracle/int5.py.
 
-Gate: ||y - y_ref||_F / ||y_ref||_F <= 2e-3 overall and per partition against the fp64
-reference on the same activation codes, rows past M never written (sentinel-checked), at the
-decode shapes (M = 1, 8), the merged-QKV shape (three partitions), the gate_up prefill shape
-(sampled rows) and ragged shapes. The packed SZ words are checked against their definition.
+Gates (tests/parity.py): Frobenius 2e-3 overall and per partition and the element-wise bound
+against the fp64 reference on the same activation codes, rows past M never written
+(sentinel-checked), at the decode shapes (M = 1, 8), the merged-QKV shape (three partitions), the
+gate_up prefill shape (all 2048 rows), one-signed activations and ragged shapes. The packed SZ
+words are checked against their definition.
 """
 import numpy as np
 import pytest
@@ -16,11 +17,11 @@ from oracle import gemm as ogemm
 from oracle import int5 as oint5
 from oracle import prologue as opro
 
+import parity
 from gpu_util import SENT_BF16, bf16_to_f64, prologue_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-3
 EXTRA_ROWS = 3
 
 
@@ -39,14 +40,10 @@ def _run(A, S, R, wpk, sz, N, pb1, pb2):
     return ybuf[:M]
 
 
-def _check(name, y, y_ref, bounds, N):
-    rel = ogemm.rel_frobenius(y, y_ref)
-    pb1, pb2 = bounds
-    edges = [0] + [b for b in (pb1, pb2) if b < N] + [N]
-    parts = [ogemm.rel_frobenius(y[:, a:b], y_ref[:, a:b]) for a, b in zip(edges[:-1], edges[1:])]
-    print(f"[gemm5 {name}] rel={rel:.3e} per-partition={[f'{p:.3e}' for p in parts]}", flush=True)
-    assert np.all(np.isfinite(y))
-    assert rel <= TOL and max(parts) <= TOL
+def _check(name, y, A, S, w, wl):
+    y_ref = oint5.gemm_ref5(A, S, w.qweight, w.qweight_hi, w.qzeros, w.qzeros_hi, w.scales, *wl.bounds)
+    mags = parity.magnitudes_int5(A, S, w, *wl.bounds)
+    parity.check(f"gemm5 {name}", y, y_ref, mags, wl.bounds, wl.G)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode_m1", "decode_m8", "qkv", "prefill"])
@@ -55,21 +52,25 @@ def test_gemm5_parity(name):
     print(f"[gemm5 {name}] M={wl.M} K={wl.K} N={wl.N} P={wl.P}", flush=True)
     x = synth.activations(wl)
     pl, tl, cl = synth.rotations(wl)
-    if wl.M <= 64:
-        rows = np.arange(wl.M)
-        A, S, R = opro.rotate_quant(x, pl, tl, cl)
-        Ad, Sd, Rd = to_dev(A), to_dev(S), to_dev(R)
-        Aref, Sref = A, S
-    else:
-        # GPU prologue for all rows; the oracle's codes for a row sample (bit-equal, pinned elsewhere)
-        Ad, Sd, Rd = prologue_gpu(wl, x, pl, tl, cl)
-        rows = np.sort(np.random.default_rng(21).choice(wl.M, 48, replace=False))
-        Aref, Sref, _ = opro.rotate_quant(x[rows], pl, tl, cl)
+    A, S, R = opro.rotate_quant(x, pl, tl, cl)
     w = synth.weights5(wl)
     wpk, sz = _pack5(w)
-    y = _run(Ad, Sd, Rd, wpk, sz, wl.N, *wl.bounds)
-    y_ref = oint5.gemm_ref5(Aref, Sref, w.qweight, w.qweight_hi, w.qzeros, w.qzeros_hi, w.scales, *wl.bounds)
-    _check(name, bf16_to_f64(y)[rows], y_ref, wl.bounds, wl.N)
+    y = _run(to_dev(A), to_dev(S), to_dev(R), wpk, sz, wl.N, *wl.bounds)
+    _check(name, bf16_to_f64(y), A, S, w, wl)
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_gemm5_one_signed_activations(M):
+    """Identity rotations on |N(0,1)| activations with outliers: one-signed codes (decode and
+    prefill kernels)."""
+    wl = synth.Workload("onesigned5", 175, M, 1024, 2048)
+    x = synth.activations_one_signed(wl)
+    pl, tl, cl = synth.rotations_identity(wl)
+    A, S, R = opro.rotate_quant(x, pl, tl, cl)
+    w = synth.weights5(wl)
+    wpk, sz = _pack5(w)
+    y = _run(to_dev(A), to_dev(S), to_dev(R), wpk, sz, wl.N, *wl.bounds)
+    _check(f"one-signed M={M}", bf16_to_f64(y), A, S, w, wl)
 
 
 @pytest.mark.parametrize("M,K,N,splits", [
@@ -86,8 +87,7 @@ def test_gemm5_ragged_shapes(M, K, N, splits):
     w = synth.weights5(wl)
     wpk, sz = _pack5(w)
     y = _run(to_dev(A), to_dev(S), to_dev(R), wpk, sz, N, *wl.bounds)
-    y_ref = oint5.gemm_ref5(A, S, w.qweight, w.qweight_hi, w.qzeros, w.qzeros_hi, w.scales, *wl.bounds)
-    _check(f"ragged M={M} K={K} N={N}", bf16_to_f64(y), y_ref, wl.bounds, N)
+    _check(f"ragged M={M} K={K} N={N}", bf16_to_f64(y), A, S, w, wl)
 
 
 def test_packed_sz5_definition():

@@ -2,7 +2,8 @@
 
 Prologue: int8 codes, group scales and row-sums bitwise equal to the oracle, guards untouched, on
 every workload (sampled rows at 8192) and on ragged / zero / saturating / strided inputs. GEMM:
-||y - y_ref||_F / ||y_ref||_F <= 2e-3 overall and per partition, rows past M never written.
+the gates of tests/parity.py (Frobenius 2e-3 overall and per partition, element-wise bound), all
+rows up to 2048, one-signed activations, rows past M never written.
 """
 import numpy as np
 import pytest
@@ -13,11 +14,11 @@ import synth
 from oracle import gemm as ogemm
 from oracle import int8 as oi8
 
+import parity
 from gpu_util import SENT_BF16, SENT_F32, SENT_U8, bf16_to_f64, guarded, packed_weights, records_for, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-3
 EXTRA_ROWS = 3
 SAMPLE_ROWS = 192
 
@@ -91,14 +92,10 @@ def _run_gemm_i8(A, S, R, wpk, sz, N, pb1, pb2):
     return ybuf[:M]
 
 
-def _check(name, y, y_ref, bounds, N):
-    rel = ogemm.rel_frobenius(y, y_ref)
-    pb1, pb2 = bounds
-    edges = [0] + [b for b in (pb1, pb2) if b < N] + [N]
-    parts = [ogemm.rel_frobenius(y[:, a:b], y_ref[:, a:b]) for a, b in zip(edges[:-1], edges[1:])]
-    print(f"[i8 gemm {name}] rel={rel:.3e} per-partition={[f'{p:.3e}' for p in parts]}", flush=True)
-    assert np.all(np.isfinite(y))
-    assert rel <= TOL and max(parts) <= TOL
+def _check(name, y, A, S, w, wl):
+    y_ref = oi8.gemm_ref_i8(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds)
+    mags = parity.magnitudes_int4(A, S, w, *wl.bounds, act="int8")
+    parity.check(f"i8 gemm {name}", y, y_ref, mags, wl.bounds, wl.G)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode_m1", "decode_m8", "qkv", "prefill"])
@@ -111,9 +108,21 @@ def test_gemm_i8_parity(name):
     w = synth.weights(wl)
     wpk, sz = packed_weights(w)
     y = _run_gemm_i8(to_dev(A), to_dev(S), to_dev(R), wpk, sz, wl.N, *wl.bounds)
-    rows = np.arange(wl.M) if wl.M <= 64 else np.random.default_rng(18).choice(wl.M, 64, replace=False)
-    y_ref = oi8.gemm_ref_i8(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds, rows=rows)
-    _check(name, bf16_to_f64(y)[rows], y_ref, wl.bounds, wl.N)
+    _check(name, bf16_to_f64(y), A, S, w, wl)
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_gemm_i8_one_signed_activations(M):
+    """Identity rotations on |N(0,1)| activations with outliers: one-signed int8 codes."""
+    wl = synth.Workload("onesigned8", 115, M, 1024, 2048)
+    x = synth.activations_one_signed(wl)
+    pl, tl, cl = synth.rotations_identity(wl)
+    A, S, R = oi8.rotate_quant_i8(x, pl, tl, cl)
+    assert np.all(A >= 0)
+    w = synth.weights(wl)
+    wpk, sz = packed_weights(w)
+    y = _run_gemm_i8(to_dev(A), to_dev(S), to_dev(R), wpk, sz, wl.N, *wl.bounds)
+    _check(f"one-signed M={M}", bf16_to_f64(y), A, S, w, wl)
 
 
 @pytest.mark.parametrize("name", ["full_gate_up", "full_down"])
@@ -126,10 +135,9 @@ def test_i8_end_to_end_full_shapes(name):
     w = synth.weights(wl)
     wpk, sz = packed_weights(w)
     y = _run_gemm_i8(A, S, R, wpk, sz, wl.N, *wl.bounds)
-    rows = np.sort(np.concatenate([[0, wl.M - 1], np.random.default_rng(28).choice(np.arange(1, wl.M - 1), 30, replace=False)]))
+    rows = np.sort(np.concatenate([[0, wl.M - 1], np.random.default_rng(28).choice(np.arange(1, wl.M - 1), 62, replace=False)]))
     Ar, Sr, _ = oi8.rotate_quant_i8(x[rows], pl, tl, cl)
-    y_ref = oi8.gemm_ref_i8(Ar, Sr, w.qweight, w.qzeros, w.scales, *wl.bounds)
-    _check(name, bf16_to_f64(y)[rows], y_ref, wl.bounds, wl.N)
+    _check(name, bf16_to_f64(y)[rows], Ar, Sr, w, wl)
 
 
 @pytest.mark.parametrize("M,K,N,splits", [
@@ -144,5 +152,4 @@ def test_gemm_i8_ragged_shapes(M, K, N, splits):
     w = synth.weights(wl)
     wpk, sz = packed_weights(w)
     y = _run_gemm_i8(to_dev(A), to_dev(S), to_dev(R), wpk, sz, N, *wl.bounds)
-    y_ref = oi8.gemm_ref_i8(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds)
-    _check(f"ragged M={M} K={K} N={N}", bf16_to_f64(y), y_ref, wl.bounds, N)
+    _check(f"ragged M={M} K={K} N={N}", bf16_to_f64(y), A, S, w, wl)

@@ -3,8 +3,9 @@
 Prologue: codes, token scales and row-sums bitwise equal to the oracle (scales and row-sums as
 uint32 bit patterns), guard regions past the outputs untouched, on every workload (sampled rows
 for the 8192-row ones), plus ragged, zero, saturating, strided and 4-byte-aligned inputs. GEMM:
-||y - y_ref||_F / ||y_ref||_F <= 2e-3 overall and per partition against the fp64 reference,
-rows past M never written.
+the gates of tests/parity.py (Frobenius 2e-3 overall and per partition, element-wise bound)
+against the fp64 reference, all rows up to 2048, one-signed activations, rows past M never
+written.
 """
 import numpy as np
 import pytest
@@ -15,11 +16,11 @@ import synth
 from oracle import gemm as ogemm
 from oracle import tokquant as otok
 
+import parity
 from gpu_util import SENT_BF16, SENT_F32, SENT_U8, bf16_to_f64, guarded, packed_weights, records_for, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-3
 EXTRA_ROWS = 3
 SAMPLE_ROWS = 192
 
@@ -112,14 +113,10 @@ def _run_gemm_tok(A, S, R, wpk, sz, N, pb1, pb2):
     return ybuf[:M]
 
 
-def _check(name, y, y_ref, bounds, N):
-    rel = ogemm.rel_frobenius(y, y_ref)
-    pb1, pb2 = bounds
-    edges = [0] + [b for b in (pb1, pb2) if b < N] + [N]
-    parts = [ogemm.rel_frobenius(y[:, a:b], y_ref[:, a:b]) for a, b in zip(edges[:-1], edges[1:])]
-    print(f"[tok gemm {name}] rel={rel:.3e} per-partition={[f'{p:.3e}' for p in parts]}", flush=True)
-    assert np.all(np.isfinite(y))
-    assert rel <= TOL and max(parts) <= TOL
+def _check(name, y, A, S, w, wl):
+    y_ref = otok.gemm_ref_tok(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds)
+    mags = parity.magnitudes_int4(A, S, w, *wl.bounds, tok=True)
+    parity.check(f"tok gemm {name}", y, y_ref, mags, wl.bounds, wl.G)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode_m1", "decode_m8", "qkv", "prefill"])
@@ -132,9 +129,21 @@ def test_gemm_tok_parity(name):
     w = synth.weights(wl)
     wpk, sz = packed_weights(w)
     y = _run_gemm_tok(to_dev(A), to_dev(S), to_dev(R), wpk, sz, wl.N, *wl.bounds)
-    rows = np.arange(wl.M) if wl.M <= 64 else np.random.default_rng(8).choice(wl.M, 64, replace=False)
-    y_ref = otok.gemm_ref_tok(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds, rows=rows)
-    _check(name, bf16_to_f64(y)[rows], y_ref, wl.bounds, wl.N)
+    _check(name, bf16_to_f64(y), A, S, w, wl)
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_gemm_tok_one_signed_activations(M):
+    """Identity rotations on |N(0,1)| activations with outliers: one-signed codes."""
+    wl = synth.Workload("onesignedtok", 105, M, 1024, 2048)
+    x = synth.activations_one_signed(wl)
+    pl, tl, cl = synth.rotations_identity(wl)
+    A, S, R = otok.rotate_quant_tok(x, pl, tl, cl)
+    assert np.all(A < 0x80)
+    w = synth.weights(wl)
+    wpk, sz = packed_weights(w)
+    y = _run_gemm_tok(to_dev(A), to_dev(S), to_dev(R), wpk, sz, wl.N, *wl.bounds)
+    _check(f"one-signed M={M}", bf16_to_f64(y), A, S, w, wl)
 
 
 @pytest.mark.parametrize("name", ["full_gate_up", "full_down"])
@@ -147,10 +156,9 @@ def test_tok_end_to_end_full_shapes(name):
     w = synth.weights(wl)
     wpk, sz = packed_weights(w)
     y = _run_gemm_tok(A, S, R, wpk, sz, wl.N, *wl.bounds)
-    rows = np.sort(np.concatenate([[0, wl.M - 1], np.random.default_rng(9).choice(np.arange(1, wl.M - 1), 30, replace=False)]))
+    rows = np.sort(np.concatenate([[0, wl.M - 1], np.random.default_rng(9).choice(np.arange(1, wl.M - 1), 62, replace=False)]))
     Ar, Sr, _ = otok.rotate_quant_tok(x[rows], pl, tl, cl)
-    y_ref = otok.gemm_ref_tok(Ar, Sr, w.qweight, w.qzeros, w.scales, *wl.bounds)
-    _check(name, bf16_to_f64(y)[rows], y_ref, wl.bounds, wl.N)
+    _check(name, bf16_to_f64(y)[rows], Ar, Sr, w, wl)
 
 
 @pytest.mark.parametrize("M,K,N,splits", [
@@ -165,5 +173,4 @@ def test_gemm_tok_ragged_shapes(M, K, N, splits):
     w = synth.weights(wl)
     wpk, sz = packed_weights(w)
     y = _run_gemm_tok(to_dev(A), to_dev(S), to_dev(R), wpk, sz, N, *wl.bounds)
-    y_ref = otok.gemm_ref_tok(A, S, w.qweight, w.qzeros, w.scales, *wl.bounds)
-    _check(f"ragged M={M} K={K} N={N}", bf16_to_f64(y), y_ref, wl.bounds, N)
+    _check(f"ragged M={M} K={K} N={N}", bf16_to_f64(y), A, S, w, wl)
