@@ -248,8 +248,11 @@ int pq_gemm5(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, i
  *        or w (gemma == 0), all in binary32 (the row's sum of squares in a fixed order)
  *   A, ASG, RS = pq_rotate_quant of hs (same arithmetic, every partition).
  *
- * x_d, res_d  f16 [M, ldx] / [M, ldr] (first K columns used); res_out_d f16 [M, ldo] (may be
- *             res_d itself: each element is read before it is written); w_d f16 [K].
+ * x_d, res_d  f16 [M, ldx] / [M, ldr] (first K columns used); res_out_d f16 [M, ldo]: either
+ *             disjoint from res_d's rows, or res_d itself with ldo == ldr (in place; the launch
+ *             then keeps one workgroup per 4 tokens, which at M <= 64 is slower than the split form
+ *             a separate res_out gets). Any other overlap returns PQ_ERR_SHAPE. No other output
+ *             may overlap an input. w_d f16 [K].
  * hs_d        out f16 [M, K] contiguous.
  * rec_d, cs_d, a_d, asg_d, rs_d  as pq_rotate_quant.
  * eps > 0 and finite; 1 <= P <= 3; K % 128 == 0 and K <= 18432 (each row is kept on chip);

@@ -438,7 +438,8 @@ __global__ __launch_bounds__(64 * kTokWaves) void add_rms_rotate_quant_kernel(
   auto mine = [&](int j) { return !kChunked || j == chunk; };
 
   // residual add; the new residual is stored as the page's producer returns it (res_out may be
-  // res itself: each element is read before the same lane writes it)
+  // res itself only in the unchunked form, where each element is read before the same lane writes
+  // it; chunks read the whole row, so the launcher never runs them in place)
   uint32_t hp[NPG][4];
   float ss = 0.0f;
 #pragma unroll
@@ -690,9 +691,19 @@ int pq_add_rms_rotate_quant(const uint16_t* x_d, int64_t ldx, const uint16_t* re
     return set_error(PQ_ERR_ALIGN, "%s: misaligned pointer", what);
   const int G = K / PQ_GROUP;
   const int npg = (G + kTokWaves - 1) / kTokWaves;
+  // The new residual may replace the old one in place (res_out_d == res_d, ldo == ldr); any other
+  // overlap of the two row ranges is rejected.
+  const uintptr_t r0 = reinterpret_cast<uintptr_t>(res_d), o0 = reinterpret_cast<uintptr_t>(res_out_d);
+  const uintptr_t r1 = r0 + 2 * (static_cast<uintptr_t>(M - 1) * static_cast<uintptr_t>(ldr) + static_cast<uintptr_t>(K));
+  const uintptr_t o1 = o0 + 2 * (static_cast<uintptr_t>(M - 1) * static_cast<uintptr_t>(ldo) + static_cast<uintptr_t>(K));
+  const bool inplace = r0 < o1 && o0 < r1;
+  if (inplace && (o0 != r0 || ldo != ldr))
+    return set_error(PQ_ERR_SHAPE, "%s: res_out overlaps res without being the same rows (res_out == res and ldo == ldr)", what);
   // few tokens: one workgroup per (quad, chunk of 16 groups), each reading the whole row for its
-  // sum of squares; many tokens: one workgroup per quad (no row read twice)
-  const bool chunked = M <= 64;
+  // sum of squares; many tokens, or an in-place residual: one workgroup per quad. In the chunked
+  // form every chunk reads residual elements that other chunks write, so it cannot run in place;
+  // with one workgroup per quad each element is read by the lane that later writes it.
+  const bool chunked = M <= 64 && !inplace;
   const int64_t blocks = static_cast<int64_t>((M + 3) / 4) * (chunked ? npg : 1);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint2* rec = static_cast<const uint2*>(rec_d);

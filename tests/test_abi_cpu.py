@@ -222,6 +222,12 @@ def test_add_rms_rotate_quant_validation():
     assert call(P=4) == -4
     assert call(r=None) == -1 and call(hs=None) == -1
     assert call(x=ctypes.c_void_p(0x100008)) == -3
+    # the new residual overlapping the old one other than as the same rows: rejected before launch
+    assert call(ro=ctypes.c_void_p(0x100000 + 512)) == -2                  # one row further on
+    assert call(ro=ctypes.c_void_p(0x100000 + 16)) == -2                   # inside the first row
+    assert call(ldo=264) == -2                                             # same start, other stride
+    assert call(r=ctypes.c_void_p(0x100000 + 3 * 512)) == -2               # res starts in res_out's rows
+    assert "overlaps" in pq.lib().pq_last_error().decode()
 
 
 def _rq(**kw):

@@ -104,3 +104,32 @@ def test_producer_plain_inplace_and_cancelled_rows():
     out = _run(wl, x, r, w, pl, tl, cl, inplace=True)
     _check("in-place", wl, x, r, w, pl, tl, cl, out)
     assert not out[1][2].any() and not out[2][:, 2].any() and not out[3][:, 2].any()
+
+
+@pytest.mark.parametrize("M,K", [(1, 5120), (8, 5120), (37, 5120), (8, 17408)])
+def test_producer_inplace_residual(M, K):
+    """res_out == res at the token counts that use several workgroups per token quad when the
+    residual goes elsewhere (M <= 64): the in-place call must equal the oracle (and so the
+    out-of-place call) bit for bit."""
+    wl = synth.Workload("prodinplace", 210 + M + K // 128, M, K, 128)
+    print(f"[producer in-place] M={M} K={K}", flush=True)
+    x, r, w = synth.activations(wl), synth.residual(wl), synth.norm_weight(wl)
+    pl, tl, cl = synth.rotations(wl)
+    out_sep = _run(wl, x, r, w, pl, tl, cl)
+    out_inp = _run(wl, x, r, w, pl, tl, cl, inplace=True)
+    _check(f"in-place M={M} K={K}", wl, x, r, w, pl, tl, cl, out_inp)
+    for a, b in zip(out_sep, out_inp):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_producer_rejects_partial_residual_overlap():
+    """res_out shifted by one row inside res: rejected before any launch, outputs untouched."""
+    M, K = 8, 256
+    res = torch.zeros((M + 1, K), dtype=torch.float16, device="cuda")
+    x = torch.zeros((M, K), dtype=torch.float16, device="cuda")
+    w = torch.zeros(K, dtype=torch.float16, device="cuda")
+    rec = torch.zeros((1, 8, K // 2, 8), dtype=torch.uint8, device="cuda")
+    cs = torch.zeros((1, K), dtype=torch.float16, device="cuda")
+    with pytest.raises(pq.PQError) as e:
+        pq.add_rms_rotate_quant(x, res[:M], w, EPS, rec, cs, residual_out=res[1:M + 1])
+    assert e.value.code == -2
