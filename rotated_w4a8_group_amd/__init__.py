@@ -115,6 +115,67 @@ def _need(t, dtype, name):
         raise TypeError(f"{name}: expected a contiguous CUDA tensor of {dtype}")
 
 
+def _validate(specs, rows=()):
+    """Checks every argument the C ABI cannot see before anything is called.
+
+    specs: (tensor, name, dtype, shape) for contiguous tensors, where shape is a tuple or an int
+    (a minimum number of elements). rows: (tensor, name, dtype, (M, K)) for row-strided 2-D
+    tensors (unit column stride). Dtypes and shapes of all of them are checked first (TypeError /
+    ValueError), then that each is a CUDA tensor on the first one's device (TypeError), so a
+    shape mismatch is reported the same way whatever the devices."""
+    import torch
+    for t, name, dtype, shape in list(specs) + list(rows):
+        if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+            raise TypeError(f"{name}: expected a tensor of {dtype}")
+    for t, name, dtype, shape in specs:
+        if isinstance(shape, tuple):
+            if tuple(t.shape) != tuple(int(d) for d in shape):
+                raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+        elif t.numel() < shape:
+            raise ValueError(f"{name}: {t.numel()} elements, at least {shape} needed")
+    for t, name, dtype, shape in rows:
+        if t.dim() != 2 or tuple(t.shape) != tuple(shape) or t.stride(1) != 1:
+            raise ValueError(f"{name}: expected a [{shape[0]}, {shape[1]}] tensor with unit column stride, "
+                             f"got shape {tuple(t.shape)} strides {t.stride()}")
+    devs = set()
+    for t, name, dtype, shape in list(specs) + list(rows):
+        if not t.is_cuda:
+            raise TypeError(f"{name}: expected a CUDA tensor")
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise TypeError(f"tensors on several devices: {sorted(str(d) for d in devs)}")
+    for t, name, dtype, shape in specs:
+        if not t.is_contiguous():
+            raise TypeError(f"{name}: expected a contiguous tensor")
+
+
+def _partitions(cs, K):
+    """P from the channel-scale tensor: [P, K] or [K] (one partition)."""
+    if cs.dim() == 2:
+        return cs.shape[0]
+    if cs.dim() == 1:
+        return 1
+    raise ValueError(f"cs: expected [P, K] or [K], got shape {tuple(cs.shape)}")
+
+
+def _prologue_specs(x, rec, cs, K):
+    """The inputs every prologue shares: x [M, K] rows, records [P][8][K/2] (8 bytes each),
+    channel scales [P, K]; returns (P, specs, rows)."""
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x: expected a [M, K] tensor")
+    if K <= 0 or K % GROUP:
+        raise ValueError(f"x: K={K} must be a positive multiple of {GROUP}")
+    P = _partitions(cs, K)
+    if not 1 <= P <= 3:
+        raise ValueError(f"cs: {P} partitions, expected 1..3")
+    rec_shape = (P, LAYERS, K // 2, 8) if rec.dim() == 4 else (LAYERS, K // 2, 8)
+    if rec.dim() == 3 and P != 1:
+        raise ValueError("rec: a [8, K/2, 8] record set serves one partition only")
+    cs_shape = (P, K) if cs.dim() == 2 else (K,)
+    return P, [(rec, "rec", torch.uint8, rec_shape), (cs, "cs", torch.float16, cs_shape)]
+
+
 # ------------------------------------------------------------------------------------------
 def build_records(pairs, theta):
     """pairs int16 [8, K], theta f16 [8, K/2] (numpy, host) -> uint8 [8, K/2, 8] records."""
@@ -153,10 +214,13 @@ def pack_weights(qweight, qzeros, scales, stream=None):
     """AWQ qweight int32 [K, N/8], qzeros int32 [K/128, N/8], scales f16 [K/128, N] (CUDA)
     -> (wpk uint8 [K*N/2], sz f16 [K/128, N, 2])."""
     import torch
-    _need(qweight, torch.int32, "qweight")
-    _need(qzeros, torch.int32, "qzeros")
-    _need(scales, torch.float16, "scales")
+    if not isinstance(qweight, torch.Tensor) or qweight.dim() != 2:
+        raise ValueError("qweight: expected an int32 [K, N/8] tensor")
     K, N = qweight.shape[0], qweight.shape[1] * 8
+    if K % GROUP or N % 16 or K == 0:
+        raise ValueError(f"qweight: K={K} must be a multiple of {GROUP} and N={N} of 16")
+    _validate([(qweight, "qweight", torch.int32, (K, N // 8)), (qzeros, "qzeros", torch.int32, (K // GROUP, N // 8)),
+               (scales, "scales", torch.float16, (K // GROUP, N))])
     wpk = torch.empty(lib().pq_packed_weight_bytes(K, N), dtype=torch.uint8, device=qweight.device)
     sz = torch.empty((K // GROUP, N, 2), dtype=torch.float16, device=qweight.device)
     _check("pq_pack_weights", lib().pq_pack_weights(
@@ -169,12 +233,15 @@ def pack_weights5(qweight, qweight_hi, qzeros, qzeros_hi, scales, stream=None):
     [K/128, N/8], qzeros_hi int32 [K/128, N/32], scales f16 [K/128, N] (CUDA)
     -> (wpk5 uint8 [pq_packed_weight5_bytes], sz f16 [K/128, N, 2])."""
     import torch
-    for t, name in ((qweight, "qweight"), (qweight_hi, "qweight_hi"), (qzeros, "qzeros"), (qzeros_hi, "qzeros_hi")):
-        _need(t, torch.int32, name)
-    _need(scales, torch.float16, "scales")
+    if not isinstance(qweight, torch.Tensor) or qweight.dim() != 2:
+        raise ValueError("qweight: expected an int32 [K, N/8] tensor")
     K, N = qweight.shape[0], qweight.shape[1] * 8
-    if tuple(qweight_hi.shape) != (K, N // 32) or tuple(qzeros_hi.shape) != (K // GROUP, N // 32):
-        raise TypeError("qweight_hi / qzeros_hi: expected [K, N/32] / [K/128, N/32] int32 planes")
+    if K % GROUP or N % 32 or K == 0:
+        raise ValueError(f"qweight: K={K} must be a multiple of {GROUP} and N={N} of 32")
+    _validate([(qweight, "qweight", torch.int32, (K, N // 8)), (qweight_hi, "qweight_hi", torch.int32, (K, N // 32)),
+               (qzeros, "qzeros", torch.int32, (K // GROUP, N // 8)),
+               (qzeros_hi, "qzeros_hi", torch.int32, (K // GROUP, N // 32)),
+               (scales, "scales", torch.float16, (K // GROUP, N))])
     wpk = torch.empty(max(1, lib().pq_packed_weight5_bytes(K, N)), dtype=torch.uint8, device=qweight.device)
     sz = torch.empty((K // GROUP, N, 2), dtype=torch.float16, device=qweight.device)
     _check("pq_pack_weights5", lib().pq_pack_weights5(
@@ -183,75 +250,87 @@ def pack_weights5(qweight, qweight_hi, qzeros, qzeros_hi, scales, stream=None):
     return wpk, sz
 
 
+def _rotate_quant_common(fn, x, rec, cs, out, stream, a_dtype, tok=False):
+    """Checks x [M, K], the records and channel scales, and caller-given outputs (codes [P, M, K],
+    scales [P, M, G] or [P, M] with tok, row-sums [P, M, G]); allocates missing outputs."""
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x: expected a [M, K] tensor")
+    M, K = x.shape
+    P, specs = _prologue_specs(x, rec, cs, K)
+    G = K // GROUP
+    s_shape = (P, M) if tok else (P, M, G)
+    if out is not None:
+        A, S, R = out
+        specs += [(A, "A", a_dtype, (P, M, K)), (S, "AS" if tok else "ASG", torch.float32, s_shape),
+                  (R, "RS", torch.float32, (P, M, G))]
+    _validate(specs, rows=[(x, "x", torch.float16, (M, K))])
+    if out is None:
+        A = torch.empty((P, M, K), dtype=a_dtype, device=x.device)
+        S = torch.empty(s_shape, dtype=torch.float32, device=x.device)
+        R = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
+    _check(fn, getattr(lib(), fn)(
+        _ptr(x), x.stride(0), M, K, P, _ptr(rec), _ptr(cs), _ptr(A), _ptr(S), _ptr(R), _stream(stream)))
+    return A, S, R
+
+
 def rotate_quant(x, rec, cs, out=None, stream=None):
     """x f16 [M, K] (row stride may exceed K), rec uint8 [P, 8, K/2, 8] (or [8, K/2, 8]),
-    cs f16 [P, K] -> (A u8 [P, M, K], ASG f32 [P, M, G], RS f32 [P, M, G])."""
+    cs f16 [P, K] (or [K]) -> (A u8 [P, M, K], ASG f32 [P, M, G], RS f32 [P, M, G])."""
     import torch
-    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
-        raise TypeError("x: expected a CUDA float16 [M, K] tensor with unit column stride")
-    _need(rec, torch.uint8, "rec")
-    _need(cs, torch.float16, "cs")
-    M, K = x.shape
-    P = cs.shape[0] if cs.dim() == 2 else 1
-    G = K // GROUP
-    if out is None:
-        A = torch.empty((P, M, K), dtype=torch.uint8, device=x.device)
-        ASG = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
-        RS = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
-    else:
-        A, ASG, RS = out
-    _check("pq_rotate_quant", lib().pq_rotate_quant(
-        _ptr(x), x.stride(0), M, K, P, _ptr(rec), _ptr(cs), _ptr(A), _ptr(ASG), _ptr(RS), _stream(stream)))
-    return A, ASG, RS
+    return _rotate_quant_common("pq_rotate_quant", x, rec, cs, out, stream, torch.uint8)
 
 
 def gemm_workspace_bytes(M, N, K):
     return int(lib().pq_gemm_workspace_bytes(M, N, K))
 
 
-def gemm(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, workspace=None, stream=None):
-    """A u8 [P, M, K], ASG/RS f32 [P, M, G], packed weights -> y bf16 [M, N] (or into ``out``,
-    a bf16 [M, ldy] view with unit column stride)."""
+def _gemm_common(fn, A, S, RS, wpk, sz, N, pb1, pb2, out, workspace, stream, *, a_dtype, tok=False, w5=False):
+    """Checks every tensor against (P, M, K, N), allocates what is missing, calls `fn`."""
     import torch
-    _need(A, torch.uint8, "A")
-    _need(ASG, torch.float32, "ASG")
-    _need(RS, torch.float32, "RS")
-    _need(wpk, torch.uint8, "wpk")
-    _need(sz, torch.float16, "sz")
+    if not isinstance(A, torch.Tensor) or A.dim() != 3:
+        raise ValueError("A: expected a [P, M, K] tensor")
     P, M, K = A.shape
+    if K == 0 or K % GROUP:
+        raise ValueError(f"A: K={K} must be a positive multiple of {GROUP}")
+    G = K // GROUP
+    L = lib()
+    need = L.pq_packed_weight5_bytes(K, N) if w5 else L.pq_packed_weight_bytes(K, N)
+    if need == 0:
+        raise ValueError(f"N={N}: not a shape the library packs (N % {32 if w5 else 16} == 0 needed)")
+    specs = [(A, "A", a_dtype, (P, M, K)), (S, "AS" if tok else "ASG", torch.float32, (P, M) if tok else (P, M, G)),
+             (RS, "RS", torch.float32, (P, M, G)), (wpk, "wpk5" if w5 else "wpk", torch.uint8, int(need)),
+             (sz, "sz", torch.float16, (G, N, 2))]
+    ws_bytes = int(L.pq_gemm_tok_workspace_bytes(M, N, K) if tok else L.pq_gemm_workspace_bytes(M, N, K))
+    if workspace is not None:
+        specs.append((workspace, "workspace", torch.uint8, ws_bytes))
     if out is None:
+        _validate(specs)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
-        raise TypeError("out: expected a bf16 [M, ldy] tensor with unit column stride")
-    ws_bytes = gemm_workspace_bytes(M, N, K)
+    else:
+        if not isinstance(out, torch.Tensor) or out.dim() != 2 or out.shape[0] != M or out.shape[1] < N:
+            raise ValueError(f"out: expected a bf16 [{M}, >= {N}] tensor")
+        _validate(specs, rows=[(out, "out", torch.bfloat16, (M, out.shape[1]))])
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
-    _check("pq_gemm", lib().pq_gemm(
-        _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2,
+    _check(fn, getattr(L, fn)(
+        _ptr(A), _ptr(S), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2,
         _ptr(out), out.stride(0), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return out
+
+
+def gemm(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, workspace=None, stream=None):
+    """A u8 [P, M, K], ASG/RS f32 [P, M, G], packed weights (wpk from pack_weights, sz [G, N, 2])
+    -> y bf16 [M, N] (or into ``out``, a bf16 [M, ldy >= N] view with unit column stride)."""
+    import torch
+    return _gemm_common("pq_gemm", A, ASG, RS, wpk, sz, N, pb1, pb2, out, workspace, stream, a_dtype=torch.uint8)
 
 
 def gemm5(A, ASG, RS, wpk5, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, workspace=None, stream=None):
     """int5 bit-plane weights (from pack_weights5) with the e4m3 prologue's A/ASG/RS -> y bf16 [M, N]."""
     import torch
-    _need(A, torch.uint8, "A")
-    _need(ASG, torch.float32, "ASG")
-    _need(RS, torch.float32, "RS")
-    _need(wpk5, torch.uint8, "wpk5")
-    _need(sz, torch.float16, "sz")
-    P, M, K = A.shape
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
-        raise TypeError("out: expected a bf16 [M, ldy] tensor with unit column stride")
-    ws_bytes = gemm_workspace_bytes(M, N, K)
-    if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
-    _check("pq_gemm5", lib().pq_gemm5(
-        _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk5), _ptr(sz), N, pb1, pb2,
-        _ptr(out), out.stride(0), _ptr(workspace), _nbytes(workspace), _stream(stream)))
-    return out
+    return _gemm_common("pq_gemm5", A, ASG, RS, wpk5, sz, N, pb1, pb2, out, workspace, stream,
+                        a_dtype=torch.uint8, w5=True)
 
 
 def add_rms_rotate_quant(x, residual, weight, eps, rec, cs, gemma=True, residual_out=None, out=None, stream=None):
@@ -259,15 +338,20 @@ def add_rms_rotate_quant(x, residual, weight, eps, rec, cs, gemma=True, residual
     [P, 8, K/2, 8], cs f16 [P, K] -> (residual_out f16 [M, K] (``residual`` itself may be passed to
     update it in place), hs f16 [M, K], A u8 [P, M, K], ASG f32 [P, M, G], RS f32 [P, M, G])."""
     import torch
-    for t, name in ((x, "x"), (residual, "residual")):
-        if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
-            raise TypeError(f"{name}: expected a CUDA float16 [M, K] tensor with unit column stride")
-    _need(weight, torch.float16, "weight")
-    _need(rec, torch.uint8, "rec")
-    _need(cs, torch.float16, "cs")
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x: expected a [M, K] tensor")
     M, K = x.shape
-    P = cs.shape[0] if cs.dim() == 2 else 1
+    P, specs = _prologue_specs(x, rec, cs, K)
     G = K // GROUP
+    specs.append((weight, "weight", torch.float16, (K,)))
+    rows = [(x, "x", torch.float16, (M, K)), (residual, "residual", torch.float16, (M, K))]
+    if residual_out is not None:
+        rows.append((residual_out, "residual_out", torch.float16, (M, K)))
+    if out is not None:
+        hs, A, S, R = out
+        specs += [(hs, "hs", torch.float16, (M, K)), (A, "A", torch.uint8, (P, M, K)),
+                  (S, "ASG", torch.float32, (P, M, G)), (R, "RS", torch.float32, (P, M, G))]
+    _validate(specs, rows=rows)
     if residual_out is None:
         residual_out = torch.empty((M, K), dtype=torch.float16, device=x.device)
     if out is None:
@@ -275,8 +359,6 @@ def add_rms_rotate_quant(x, residual, weight, eps, rec, cs, gemma=True, residual
         A = torch.empty((P, M, K), dtype=torch.uint8, device=x.device)
         S = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
         R = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
-    else:
-        hs, A, S, R = out
     _check("pq_add_rms_rotate_quant", lib().pq_add_rms_rotate_quant(
         _ptr(x), x.stride(0), _ptr(residual), residual.stride(0), _ptr(weight), float(eps), 1 if gemma else 0,
         M, K, P, _ptr(rec), _ptr(cs), _ptr(residual_out), residual_out.stride(0), _ptr(hs), _ptr(A), _ptr(S),
@@ -288,66 +370,20 @@ def rotate_quant_i8(x, rec, cs, out=None, stream=None):
     """Per-group int8 mode: x f16 [M, K], rec [P, 8, K/2, 8], cs f16 [P, K] -> (A int8 [P, M, K],
     ASG f32 [P, M, G], RS f32 [P, M, G])."""
     import torch
-    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
-        raise TypeError("x: expected a CUDA float16 [M, K] tensor with unit column stride")
-    _need(rec, torch.uint8, "rec")
-    _need(cs, torch.float16, "cs")
-    M, K = x.shape
-    P = cs.shape[0] if cs.dim() == 2 else 1
-    G = K // GROUP
-    if out is None:
-        A = torch.empty((P, M, K), dtype=torch.int8, device=x.device)
-        ASG = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
-        RS = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
-    else:
-        A, ASG, RS = out
-    _check("pq_rotate_quant_i8", lib().pq_rotate_quant_i8(
-        _ptr(x), x.stride(0), M, K, P, _ptr(rec), _ptr(cs), _ptr(A), _ptr(ASG), _ptr(RS), _stream(stream)))
-    return A, ASG, RS
+    return _rotate_quant_common("pq_rotate_quant_i8", x, rec, cs, out, stream, torch.int8)
 
 
 def gemm_i8(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, workspace=None, stream=None):
     """Per-group int8 GEMM: A int8 [P, M, K], ASG/RS f32 [P, M, G], packed weights -> y bf16."""
     import torch
-    _need(A, torch.int8, "A")
-    _need(ASG, torch.float32, "ASG")
-    _need(RS, torch.float32, "RS")
-    _need(wpk, torch.uint8, "wpk")
-    _need(sz, torch.float16, "sz")
-    P, M, K = A.shape
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
-        raise TypeError("out: expected a bf16 [M, ldy] tensor with unit column stride")
-    ws_bytes = gemm_workspace_bytes(M, N, K)
-    if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
-    _check("pq_gemm_i8", lib().pq_gemm_i8(
-        _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2,
-        _ptr(out), out.stride(0), _ptr(workspace), _nbytes(workspace), _stream(stream)))
-    return out
+    return _gemm_common("pq_gemm_i8", A, ASG, RS, wpk, sz, N, pb1, pb2, out, workspace, stream, a_dtype=torch.int8)
 
 
 def rotate_quant_tok(x, rec, cs, out=None, stream=None):
     """Per-token path: x f16 [M, K], rec [P, 8, K/2, 8], cs f16 [P, K] -> (A u8 [P, M, K],
     AS f32 [P, M], RS f32 [P, M, G])."""
     import torch
-    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
-        raise TypeError("x: expected a CUDA float16 [M, K] tensor with unit column stride")
-    _need(rec, torch.uint8, "rec")
-    _need(cs, torch.float16, "cs")
-    M, K = x.shape
-    P = cs.shape[0] if cs.dim() == 2 else 1
-    G = K // GROUP
-    if out is None:
-        A = torch.empty((P, M, K), dtype=torch.uint8, device=x.device)
-        AS = torch.empty((P, M), dtype=torch.float32, device=x.device)
-        RS = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
-    else:
-        A, AS, RS = out
-    _check("pq_rotate_quant_tok", lib().pq_rotate_quant_tok(
-        _ptr(x), x.stride(0), M, K, P, _ptr(rec), _ptr(cs), _ptr(A), _ptr(AS), _ptr(RS), _stream(stream)))
-    return A, AS, RS
+    return _rotate_quant_common("pq_rotate_quant_tok", x, rec, cs, out, stream, torch.uint8, tok=True)
 
 
 def gemm_tok_workspace_bytes(M, N, K):
@@ -357,23 +393,8 @@ def gemm_tok_workspace_bytes(M, N, K):
 def gemm_tok(A, AS, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, workspace=None, stream=None):
     """Per-token GEMM: A u8 [P, M, K], AS f32 [P, M], RS f32 [P, M, G], packed weights -> y bf16."""
     import torch
-    _need(A, torch.uint8, "A")
-    _need(AS, torch.float32, "AS")
-    _need(RS, torch.float32, "RS")
-    _need(wpk, torch.uint8, "wpk")
-    _need(sz, torch.float16, "sz")
-    P, M, K = A.shape
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1:
-        raise TypeError("out: expected a bf16 [M, ldy] tensor with unit column stride")
-    ws_bytes = gemm_tok_workspace_bytes(M, N, K)
-    if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
-    _check("pq_gemm_tok", lib().pq_gemm_tok(
-        _ptr(A), _ptr(AS), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2,
-        _ptr(out), out.stride(0), _ptr(workspace), _nbytes(workspace), _stream(stream)))
-    return out
+    return _gemm_common("pq_gemm_tok", A, AS, RS, wpk, sz, N, pb1, pb2, out, workspace, stream,
+                        a_dtype=torch.uint8, tok=True)
 
 
 def e4m3_encode(q, stream=None):
