@@ -27,6 +27,70 @@ PAGES_GEMM_TFLOPS = 125.5     # the pages' GEMM alone (per-group fold v2, 2910 u
 COPY_CALIBRATION_BYTES = 64 << 20
 
 
+PROBES_SRC = os.path.join(ROOT, "bench_probes.hip")
+PROBES_LIB = os.path.join(ROOT, "bench_probes.so")
+SETTLE_MS = 300.0             # untimed steps before the timed region (the clock's ramp)
+
+
+def build_probes():
+    """Compiles the ceiling probes (bench_probes.hip) for gfx950 into bench_probes.so."""
+    import subprocess
+    tmp = PROBES_LIB + ".tmp"
+    subprocess.run(["/opt/rocm/bin/hipcc", "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PROBES_SRC, "-o", tmp], check=True)
+    os.replace(tmp, PROBES_LIB)
+    return PROBES_LIB
+
+
+def measure_ceilings(torch, np):
+    """Measured HBM read and fp8 matrix-core ceilings on this GPU (bench_probes.hip), best median
+    of 20 HIP-event-timed launches over a few launch widths, after ~100 ms of untimed launches."""
+    import ctypes
+    if not os.path.exists(PROBES_LIB):
+        raise RuntimeError(f"{PROBES_LIB} is missing: run `python __graft_entry__.py build`")
+    L = ctypes.CDLL(PROBES_LIB)
+    L.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def timed(launch, reps=20):
+        settle_clock(torch, lambda i: launch(), 8, ms=100.0)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            launch()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) * 1e-3 for a, b in ev]))
+
+    nbytes = 2 << 30                                   # 2 GiB: 8x the last-level cache
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    out = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    read = {}
+    for blocks in (1024, 2048, 4096, 8192):
+        def launch(b=blocks):
+            if L.probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, b, ctypes.c_void_p(out.data_ptr()), stream) != 0:
+                raise RuntimeError("probe_read failed")
+        read[blocks] = nbytes / timed(launch) / 1e9
+    del buf
+    mfma = {}
+    iters = 2000
+    outf = torch.empty(8192 * 256, dtype=torch.float32, device="cuda")
+    for blocks in (512, 1024, 2048):                  # 2, 4, 8 waves per SIMD on 256 CUs
+        def launch(b=blocks):
+            if L.probe_mfma(b, iters, ctypes.c_void_p(outf.data_ptr()), stream) != 0:
+                raise RuntimeError("probe_mfma failed")
+        mfma[blocks] = blocks * 4 * 8 * iters * 65536.0 / timed(launch) / 1e12
+    torch.cuda.empty_cache()
+    best_r = max(read, key=read.get)
+    best_m = max(mfma, key=mfma.get)
+    return {"hbm_read_GBs": round(read[best_r], 1), "hbm_read_blocks": best_r,
+            "fp8_mfma_TFLOPs": round(mfma[best_m], 1), "fp8_mfma_blocks": best_m,
+            "read_sweep_GBs": {str(k): round(v, 1) for k, v in read.items()},
+            "mfma_sweep_TFLOPs": {str(k): round(v, 1) for k, v in mfma.items()},
+            "probes": "bench_probes.hip: 2 GiB nontemporal 16-byte reads; 8 independent fp8 16x16x128 products per wave step"}
+
+
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_prefill_gate_up_m2048_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "rotated_w4a8_group_amd", "csrc", "pq_gemm.hip")
 
@@ -99,6 +163,9 @@ def main():
                     help="skip the per-config measurements (merged QKV M=4 P=3, M=8192 gate_up and down)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 64 MiB device copy 5 times (HBM counter calibration)")
+    ap.add_argument("--ceilings-only", action="store_true",
+                    help="only measure the HBM read and fp8 matrix-core ceilings and print them")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured ceilings")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -119,6 +186,11 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": COPY_CALIBRATION_BYTES, "launches": 5}), flush=True)
         return
+
+    if args.ceilings_only:
+        print(json.dumps({"ceilings": measure_ceilings(torch, np)}), flush=True)
+        return
+    ceilings = None if args.no_ceilings else measure_ceilings(torch, np)
 
     import rotated_w4a8_group_amd as pq
     import synth
@@ -162,6 +234,9 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # untimed steps for a fixed wall time whatever --warmup is: the clock ramps over the first
+    # tens of ms of work, and a short timed region would otherwise land on the ramp
+    settle_clock(torch, lambda i: step(i), C, ms=SETTLE_MS)
     # per-phase breakdown: eager launches with events between the two calls
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -183,6 +258,7 @@ def main():
             step(i)
     graph.replay()                      # untimed: first replay
     torch.cuda.synchronize()
+    settle_clock(torch, lambda i: graph.replay(), 1, ms=SETTLE_MS / 3)
     t0 = time.perf_counter()
     graph.replay()
     torch.cuda.synchronize()
@@ -224,7 +300,12 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "pq_gemm (zero-point pre-pass + prefill kernel)",
                      "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic()},
+        "settle_ms": SETTLE_MS,
     }
+    if ceilings is not None:
+        out["ceilings"] = ceilings
+        out["roofline"]["peak_measured"] = ceilings["fp8_mfma_TFLOPs"]
+        out["roofline"]["frac_measured"] = round(gemm_tflops / ceilings["fp8_mfma_TFLOPs"], 4)
 
     # ---- decode GEMM bandwidth (M = 1 and 8), DRAM-fed over the same weight copies. The C
     # launches (one per weight copy) are captured in one HIP graph and replayed, so the
@@ -258,6 +339,8 @@ def main():
                              "us_p90": round(float(np.percentile(t, 90)) * 1e6, 2),
                              "bytes": gemm_bytes(Md, K, N), "GBs": round(float(gbs), 1),
                              "frac_hbm": round(float(gbs) / PEAK_HBM_GBS, 4),
+                             "frac_hbm_measured": (round(float(gbs) / ceilings["hbm_read_GBs"], 4)
+                                                   if ceilings else None),
                              "timing": f"HIP graph of {C} launches over {C} weight copies, per-launch average after ~30 ms of untimed replays"}
         out["decode"] = dec
 

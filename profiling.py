@@ -2,9 +2,9 @@
 
 Used to produce the text summaries and the HBM traffic record that are kept with the sources:
 
-  python -m rotated_w4a8_group_amd.profiling summary <results.db> [--title T] [--command C]
+  python profiling.py summary <results.db> [--title T] [--command C]
       per-kernel dispatch count and average / median / min duration, as Markdown
-  python -m rotated_w4a8_group_amd.profiling traffic --fetch <db> --write <db>
+  python profiling.py traffic --fetch <db> --write <db>
           --copy-fetch <db> --copy-write <db> --kernels k1,k2 --source <file> --out <json>
       FETCH_SIZE / WRITE_SIZE per dispatch of the named kernels, scaled by what the same
       counters read for a plain copy of known size (bench.py --copy-calibration)
