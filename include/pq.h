@@ -160,6 +160,24 @@ int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, in
             int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream);
 
 /*
+ * pq_gemm without a workspace, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments, arithmetic,
+ * kernels and results as pq_gemm, minus ws_d/ws_bytes: at M > 16 the zero-point operand and the
+ * transposed group scales go to a scratch array the library holds on each device (16 MiB, from
+ * the first call on that device until the process ends), sized for the call's own P:
+ *   P * ceil(M/16) * ceil(3*(K/128)/32) KiB  +  P * (K/128) * M * 4 bytes (rounded up to 256),
+ * e.g. M = 8192 at K = 17408 for P = 1, or M = 2048 at K = 5120 for P = 3. Larger calls return
+ * PQ_ERR_SHAPE before anything is launched. Nothing is allocated; no initialisation is needed
+ * (every byte read is written earlier in the same call). All calls on one device share its
+ * scratch, so calls that overlap on a device (several streams or threads) race; serialise them.
+ * pq_gemm_noalloc_max_scratch_bytes returns the scratch size.
+ */
+size_t pq_gemm_noalloc_max_scratch_bytes(void);
+int pq_gemm_noalloc(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
+                    const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+                    int64_t ldy, pq_stream_t stream);
+
+/*
  * Per-token activation-scale path (device): the same rotation, one e4m3 scale per
  * (partition, token) instead of per (token, group) -
  *   amax = max over the whole row of |v|; as = amax * fl32(1/448); codes = e4m3(v * fl32(1/as))

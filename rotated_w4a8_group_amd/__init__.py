@@ -46,6 +46,8 @@ SIGNATURES = {
     "pq_rotate_quant": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "pq_gemm_workspace_bytes": (_SZ, [_I, _I, _I]),
     "pq_gemm": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
+    "pq_gemm_noalloc_max_scratch_bytes": (_SZ, []),
+    "pq_gemm_noalloc": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P]),
     "pq_rotate_quant_tok": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "pq_gemm_tok_workspace_bytes": (_SZ, [_I, _I, _I]),
     "pq_gemm_tok": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
@@ -324,6 +326,33 @@ def gemm(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, wor
     -> y bf16 [M, N] (or into ``out``, a bf16 [M, ldy >= N] view with unit column stride)."""
     import torch
     return _gemm_common("pq_gemm", A, ASG, RS, wpk, sz, N, pb1, pb2, out, workspace, stream, a_dtype=torch.uint8)
+
+
+def gemm_noalloc(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, stream=None):
+    """pq_gemm_noalloc: the result of ``gemm`` with the library's own per-device scratch in place of
+    a workspace (no device allocation in the call; ``out``, a bf16 [M, ldy >= N] tensor, is
+    required). Calls that overlap on one device race on that scratch."""
+    import torch
+    if out is None:
+        raise ValueError("out: gemm_noalloc writes into a caller-given bf16 [M, N] tensor")
+    if not isinstance(A, torch.Tensor) or A.dim() != 3:
+        raise ValueError("A: expected a [P, M, K] tensor")
+    P, M, K = A.shape
+    if K == 0 or K % GROUP:
+        raise ValueError(f"A: K={K} must be a positive multiple of {GROUP}")
+    G = K // GROUP
+    need = lib().pq_packed_weight_bytes(K, N)
+    if need == 0:
+        raise ValueError(f"N={N}: not a shape the library packs (N % 16 == 0 needed)")
+    if not isinstance(out, torch.Tensor) or out.dim() != 2 or out.shape[0] != M or out.shape[1] < N:
+        raise ValueError(f"out: expected a bf16 [{M}, >= {N}] tensor")
+    _validate([(A, "A", torch.uint8, (P, M, K)), (ASG, "ASG", torch.float32, (P, M, G)),
+               (RS, "RS", torch.float32, (P, M, G)), (wpk, "wpk", torch.uint8, int(need)),
+               (sz, "sz", torch.float16, (G, N, 2))], rows=[(out, "out", torch.bfloat16, (M, out.shape[1]))])
+    _check("pq_gemm_noalloc", lib().pq_gemm_noalloc(
+        _ptr(A), _ptr(ASG), _ptr(RS), M, K, P, _ptr(wpk), _ptr(sz), N, pb1, pb2, _ptr(out), out.stride(0),
+        _stream(stream)))
+    return out
 
 
 def gemm5(A, ASG, RS, wpk5, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, workspace=None, stream=None):

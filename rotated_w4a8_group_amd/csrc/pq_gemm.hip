@@ -20,6 +20,7 @@
 // in its high nibble. (w & 0x0F0F0F0F) and ((w >> 4) & 0x0F0F0F0F) are then the lane's B
 // operand registers 2q and 2q+1, matching the A operand's 32 consecutive k bytes.
 #include <algorithm>
+#include <mutex>
 
 #include "pq_device.h"
 #include "pq_internal.h"
@@ -1022,10 +1023,12 @@ namespace pq {
 // The GEMM behind pq_gemm (kTok = false: a_scale = ASG [P, M, G]), pq_gemm_tok (kTok = true:
 // a_scale = AS [P, M]), pq_gemm_i8 (kI8) and pq_gemm5 (kW5: int5 packed weights); validation is
 // the caller's.
+// ws_parts: the partition count the workspace layout is sized for (the transposed scales follow
+// the zero-point operand of that many partitions).
 template <bool kTok, bool kI8, bool kW5 = false>
 static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scale, const float* rs_d, int M, int K,
                        int P, const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
-                       int64_t ldy, void* ws_d, hipStream_t s) {
+                       int64_t ldy, void* ws_d, hipStream_t s, int ws_parts = PQ_MAX_PARTITIONS) {
   const int G = K / PQ_GROUP;
   const u32x4* wpk = static_cast<const u32x4*>(wpk_d);
   const uint32_t* sz = reinterpret_cast<const uint32_t*>(sz_d);
@@ -1063,7 +1066,7 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
   const int64_t grid = static_cast<int64_t>(map.full) + static_cast<int64_t>(map.ntiles - map.full) * map.split;
   u32x4* zpa = static_cast<u32x4*>(ws_d);
   float* asgt = kTok ? nullptr
-                     : reinterpret_cast<float*>(static_cast<uint8_t*>(ws_d) + zpe_act_bytes(M, G, PQ_MAX_PARTITIONS));
+                     : reinterpret_cast<float*>(static_cast<uint8_t*>(ws_d) + zpe_act_bytes(M, G, ws_parts));
   const int64_t zt = static_cast<int64_t>(P) * ((M + 15) / 16) * zpe_chunks(G) * 64;
   hipLaunchKernelGGL(zpe_act_kernel<kTok>, dim3(static_cast<unsigned>((zt + 255) / 256)), dim3(256), 0, s,
                      a_scale, rs_d, M, G, P, zpa, asgt);
@@ -1147,6 +1150,77 @@ int pq_gemm_i8(const int8_t* a_d, const float* asg_d, const float* rs_d, int M, 
   if (rc != PQ_OK) return rc == 1 ? PQ_OK : rc;
   return gemm_launch<false, true>("pq_gemm_i8", a8, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
                                   reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// pq_gemm_noalloc: pq_gemm for callers that cannot allocate. The prefill kernel's scratch (the
+// zero-point operand and the transposed group scales, sized for the call's own P) lives in this
+// file-scope device array instead of a caller workspace. The host side never uses the array's
+// name as an address: each device's copy is looked up once with hipGetSymbolAddress and that
+// pointer is what the kernels get. Every call on a device shares its copy, so calls that overlap
+// on one device (several streams, or threads) race on it.
+namespace pq {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on its first use). Returns PQ_OK or an error.
+static int scratch_for_current_device(const char* what, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(PQ_ERR_DEVICE, "%s: hipGetDevice failed: %s", what, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return set_error(PQ_ERR_DEVICE, "%s: device %d out of range", what, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(PQ_ERR_DEVICE, "%s: hipGetSymbolAddress(scratch) failed: %s", what, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PQ_OK;
+}
+
+// Scratch bytes pq_gemm_noalloc needs (0 at M <= 16, where the decode kernel uses none).
+static size_t noalloc_bytes(int M, int K, int P) {
+  if (M <= 16) return 0;
+  const int G = K / PQ_GROUP;
+  return zpe_act_bytes(M, G, P) + asgt_bytes(M, G, P);
+}
+
+}  // namespace pq
+
+extern "C" {
+
+size_t pq_gemm_noalloc_max_scratch_bytes(void) { return pq::kScratchBytes; }
+
+int pq_gemm_noalloc(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
+                    const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+                    int64_t ldy, pq_stream_t stream) {
+  using namespace pq;
+  clear_error();
+  // the same checks as pq_gemm, with the library's own scratch standing in for the workspace
+  const int rc = gemm_check("pq_gemm_noalloc", a_d, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy,
+                            nullptr, 0, 0);
+  if (rc != PQ_OK) return rc == 1 ? PQ_OK : rc;
+  const size_t need = noalloc_bytes(M, K, P);
+  if (need > kScratchBytes)
+    return set_error(PQ_ERR_SHAPE, "pq_gemm_noalloc: M=%d K=%d P=%d needs %zu scratch bytes, more than the %zu the "
+                     "library holds (use pq_gemm with a workspace)", M, K, P, need, kScratchBytes);
+  void* ws = nullptr;
+  if (need) {
+    const int src = scratch_for_current_device("pq_gemm_noalloc", &ws);
+    if (src != PQ_OK) return src;
+  }
+  return gemm_launch<false, false>("pq_gemm_noalloc", a_d, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy,
+                                   ws, reinterpret_cast<hipStream_t>(stream), P);
 }
 
 }  // extern "C"

@@ -189,6 +189,24 @@ def test_gemm_rejects_rows_beyond_32_bit_offsets():
     assert "too large" in pq.lib().pq_last_error().decode()
 
 
+def test_gemm_noalloc_validation_and_scratch_limit():
+    lib = pq.lib()
+    S = lib.pq_gemm_noalloc_max_scratch_bytes()
+    assert S == 16 << 20
+
+    def call(M, K, P, N=256, pb1=pq.NO_BOUNDARY, pb2=pq.NO_BOUNDARY, **kw):
+        a = dict(a=FAKE, y=FAKE)
+        a.update(kw)
+        return lib.pq_gemm_noalloc(a["a"], FAKE, FAKE, M, K, P, FAKE, FAKE, N, pb1, pb2, a["y"], N, None)
+    # beyond the scratch: rejected before anything else is touched (no device needed)
+    assert call(8192, 17408, 2, pb1=128) == -2 and "scratch" in lib.pq_last_error().decode()
+    assert call(16384, 17408, 1) == -2
+    # the same validation as pq_gemm
+    assert call(4, 100, 1) == -2 and call(4, 256, 2) == -4 and call(4, 256, 1, a=None) == -1
+    assert call(4, 256, 1, a=ctypes.c_void_p(0x100004)) == -3
+    assert call(0, 256, 1, a=None, y=None) == 0
+
+
 def test_gemm5_and_pack5_validation():
     lib = pq.lib()
     # int5 needs N % 32 == 0 (the fifth-bit planes hold 32 columns per word)
