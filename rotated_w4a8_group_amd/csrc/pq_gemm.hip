@@ -328,68 +328,82 @@ __device__ __forceinline__ void wait_vm() {
 
 // ---------------------------------------------------------------------------------------
 // decode: M <= 16, a stream of the packed weights. A CU's memory pipeline delivers a bounded
-// rate, so the kernel time is set by the CU with the most bytes: the column tiles (16 columns
-// each) are dealt out so that every CU streams the same amount. The grid is a multiple of the
-// CU count; each workgroup takes a contiguous run of 1..kDecMaxNT tiles inside one partition,
-// runs differing by at most one tile (DecodeMap). The 4 waves of a workgroup split the groups;
-// their partial sums meet in LDS at the end.
-// Each wave streams its groups through a private LDS ring of D slots with direct LDS loads: a
-// slot holds one group's NT weight tiles, the activation fragment, the SZ words and the rows'
-// asg/rs values. Group g+D-1 is requested before group g is computed and an explicit vmcnt wait
-// covers exactly group g, so D-1 groups stay in flight. The loads are invisible to the
-// compiler, which therefore never inserts waits of its own on them (register rings lose their
-// depth to such waits when the allocator copies an in-flight register). Two workgroups share a
-// CU so that two waves per SIMD hide each other's LDS and matrix-core latencies.
-constexpr int kDecWaves = 4;
-constexpr int kDecMaxNT = 6;
-constexpr int kDecRingBytes = 20480;   // per wave
-constexpr int kDecLds = kDecWaves * kDecRingBytes;
-constexpr int kDecPerCU = 2;           // workgroups resident per CU (LDS-bound)
+// rate, so the kernel time is set by the CU with the most bytes. The columns are therefore dealt
+// out in quarters of a tile (4 columns): one 8-wave workgroup per CU (its ring fills the LDS), each
+// taking a contiguous column range of the same number of quarters (gate_up N = 17408 on 256 CUs:
+// exactly 68 columns each; ranges differ by at most one quarter in general), inside one
+// partition. A range starts and ends anywhere on a 4-column line, so the tiles at its two ends are
+// loaded with the lanes of the other columns masked off (each lane owns one column of a tile
+// block) and their products for those columns are dropped. Consecutive ranges go to the same
+// XCD (workgroups are dispatched to the XCDs round-robin), so a cache line shared by two
+// neighbouring ranges is fetched once into that XCD's L2.
+// The 8 waves of a workgroup split the groups; each streams its groups through a private LDS ring
+// of D slots with direct LDS loads: a slot holds one group's tile blocks, the activation rows, the
+// SZ words and the rows' asg/rs values. Group g+D-1 is requested before group g is computed and an
+// explicit vmcnt wait covers exactly group g, so D-1 groups stay in flight. The loads are
+// invisible to the compiler, which therefore never inserts waits of its own on them (register
+// rings lose their depth to such waits when the allocator copies an in-flight register). The
+// waves' partial sums meet in LDS at the end.
+constexpr int kDecWaves = 8;
+constexpr int kDecMaxNT = 6;                       // tile blocks one range touches
+constexpr int kDecMaxQ = 4 * (kDecMaxNT - 1);      // quarters per range at most (80 columns)
+constexpr int kDecRingBytes = 20480;               // per wave
+constexpr int kDecLds = kDecWaves * kDecRingBytes; // 160 KiB: one workgroup per CU
 struct DecodeMap {
-  int wg0[4];   // first workgroup of partition q; wg0[3] = grid size
-  int t0[3];    // first tile of partition q
-  int nt[3];    // tiles of partition q
+  int wg0[4];   // first range of partition q; wg0[3] = number of ranges (the grid)
+  int c0[3];    // first column of partition q
+  int nq[3];    // quarters (4 columns) of partition q
+  int xcd;      // 1: range r = (b % 8) * (grid / 8) + b / 8 for workgroup b
 };
 
-constexpr int kDecMaxNT5 = 5;          // int5: six tiles and their planes leave no room for two slots
-template <int NT, bool kW5 = false>
+// MA = activation rows held in a slot (8 when M <= 8, else 16)
+template <int NT, int MA, bool kW5>
 struct DecodeSlot {
-  static constexpr int kSzLoads = (NT + 3) / 4;                 // 64 SZ words per load
-  static constexpr int kOffA = NT * 1024;                       // [2 halves][64 lanes][16 B]
-  static constexpr int kOffSz = (NT + 2) * 1024;                // [16 NT] words
-  static constexpr int kOffSc = kOffSz + kSzLoads * 256;        // [16] asg, [16] rs
+  static constexpr int kSzWords = 16 * NT;
+  static constexpr int kSzLoads = (kSzWords + 63) / 64;         // 64 SZ words per load
+  static constexpr int kOffA = NT * 1024;                       // [MA rows][128 B]
+  static constexpr int kOffSz = kOffA + MA * 128;               // [16 NT] words
+  static constexpr int kOffSc = kOffSz + (kSzWords * 4 + 15) / 16 * 16;   // [16] asg, [16] rs
   static constexpr int kOffH = kOffSc + 128;                    // int5: [NT][64 lanes] fifth-bit words
   static constexpr int kBytes = kOffH + (kW5 ? NT * 256 : 0);
   static constexpr int kDepth = kDecRingBytes / kBytes > 16 ? 16 : kDecRingBytes / kBytes;
-  static constexpr int kLoads = NT + 2 + kSzLoads + 2 + (kW5 ? NT : 0);   // loads per group
+  static constexpr int kLoads = NT + MA / 8 + kSzLoads + 2 + (kW5 ? NT : 0);   // loads per group
   static_assert(kDepth >= 2 && (kDepth - 1) * kLoads <= 63, "decode ring does not fit vmcnt");
 };
 
 // MR = activation rows held per lane that can be live (1 when M == 1, else 4)
-template <int NT, int MR, bool kI8, bool kW5>
+template <int NT, int MR, int MA, bool kI8, bool kW5>
 __device__ __forceinline__ void decode_body(
     const uint8_t* __restrict__ A, const float* __restrict__ asgp, const float* __restrict__ rsp,
     int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ hi,
-    const uint32_t* __restrict__ sz, int N, int p, int tfirst, uint16_t* __restrict__ y, int64_t ldy,
+    const uint32_t* __restrict__ sz, int N, int p, int c0, int c1, uint16_t* __restrict__ y, int64_t ldy,
     uint8_t* smem) {
-  using S = DecodeSlot<NT, kW5>;
+  using S = DecodeSlot<NT, MA, kW5>;
   constexpr int D = S::kDepth;
   const int G = K >> 7;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
   const int col = lane & 15, kq = lane >> 4;
-  const int n0 = 16 * tfirst;
+  const int tfirst = c0 >> 4, n0 = 16 * tfirst;
   const int g0 = (G * wave) / kDecWaves, g1 = (G * (wave + 1)) / kDecWaves;
 
-  // Sources: a scalar base per group plus a fixed per-lane offset. A operand row = lane % 16:
-  // lanes with row >= M load nothing and their products land in output rows that are never
-  // stored; the same holds for scale rows >= M.
+  // Sources: a scalar base per group plus a fixed per-lane offset. Weight tile t: every lane owns
+  // column n0 + 16t + lane % 16; lanes whose column is outside [c0, c1) load nothing (each tile
+  // keeps at least 4 columns, so every load has live lanes in every wave and is counted by
+  // vmcnt). Activation rows: lane l loads 16 bytes of row l / 8 (rows past M repeat row M - 1).
   const uint8_t* wbase = reinterpret_cast<const uint8_t*>(wpk) + static_cast<size_t>(tfirst) * G * 1024;
   const uint32_t woff = 16 * lane;
+  bool won[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int n = n0 + 16 * t + col;
+    won[t] = n >= c0 && n < c1;
+  }
   const uint8_t* hbase = reinterpret_cast<const uint8_t*>(hi) + static_cast<size_t>(tfirst) * G * 256;
-  const bool a_on = col < M;
   const uint8_t* abase = A + static_cast<size_t>(p) * M * K;
-  const uint32_t aoff = static_cast<uint32_t>((a_on ? col : 0) * K + 32 * kq);
+  const int ar0 = min(lane >> 3, M - 1), ar1 = min((lane >> 3) + 8, M - 1);
+  const uint32_t aoff0 = static_cast<uint32_t>(ar0 * K + 16 * (lane & 7));
+  const uint32_t aoff1 = static_cast<uint32_t>(ar1 * K + 16 * (lane & 7));
   const uint8_t* zbase = reinterpret_cast<const uint8_t*>(sz + n0);
   const uint32_t zoff = 4 * lane;
   const int srow = lane & 15;
@@ -402,31 +416,30 @@ __device__ __forceinline__ void decode_body(
     const uint32_t sb = ring + slot * S::kBytes;
     const uint8_t* wg = wbase + static_cast<size_t>(g) * 1024;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) lds_dma16_s(wg + static_cast<size_t>(t) * G * 1024, woff, sb + t * 1024);
+    for (int t = 0; t < NT; ++t)
+      if (won[t]) lds_dma16_s(wg + static_cast<size_t>(t) * G * 1024, woff, sb + t * 1024);
     if constexpr (kW5) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        lds_dma4_s(hbase + (static_cast<size_t>(t) * G + g) * 256, 4 * lane, sb + S::kOffH + t * 256);
+        if (won[t]) lds_dma4_s(hbase + (static_cast<size_t>(t) * G + g) * 256, 4 * lane, sb + S::kOffH + t * 256);
     }
-    if (a_on) {
-      lds_dma16_s(abase + 128 * g, aoff, sb + S::kOffA);
-      lds_dma16_s(abase + 128 * g + 16, aoff, sb + S::kOffA + 1024);
-    }
+    lds_dma16_s(abase + 128 * g, aoff0, sb + S::kOffA);
+    if constexpr (MA == 16) lds_dma16_s(abase + 128 * g, aoff1, sb + S::kOffA + 1024);
     const uint8_t* zg = zbase + static_cast<size_t>(g) * N * 4;
 #pragma unroll
     for (int j = 0; j < S::kSzLoads; ++j)
-      if (lane + 64 * j < 16 * NT) lds_dma4_s(zg + 256 * j, zoff, sb + S::kOffSz + j * 256);
+      if (lane + 64 * j < S::kSzWords) lds_dma4_s(zg + 256 * j, zoff, sb + S::kOffSz + j * 256);
     if (as_on) lds_dma4_s(asgp + g, soff, sb + S::kOffSc);
     if (rs_on) lds_dma4_s(rsp + g, soff, sb + S::kOffSc);
   };
-  // Each load above has a live lane in every wave (lane 0 for weights, A, SZ and asg; lane 16
-  // for rs), so each one is issued and counted by vmcnt.
   const int ng = g1 - g0;
   for (int i = 0; i < D - 1 && i < ng; ++i) issue(g0 + i, i);
 
   v4f acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  // MFMA A operand: lane l takes row l % 16 (folded onto the MA rows held), k 32 (l / 16) .. + 31
+  const int arow = (lane & 15) & (MA - 1);
   int slot = 0;
   for (int g = g0; g < g1; ++g) {
     if (g + D - 1 < g1) {
@@ -436,8 +449,8 @@ __device__ __forceinline__ void decode_body(
       wait_vm<0>();
     }
     const uint8_t* sp = ringp + slot * S::kBytes;
-    const u32x4 a0 = *reinterpret_cast<const u32x4*>(sp + S::kOffA + 16 * lane);
-    const u32x4 a1 = *reinterpret_cast<const u32x4*>(sp + S::kOffA + 1024 + 16 * lane);
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(sp + S::kOffA + arow * 128 + 32 * kq);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(sp + S::kOffA + arow * 128 + 32 * kq + 16);
     const v8i av = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     const v4f as = *reinterpret_cast<const v4f*>(sp + S::kOffSc + 16 * kq);
     const v4f rs = *reinterpret_cast<const v4f*>(sp + S::kOffSc + 64 + 16 * kq);
@@ -455,45 +468,51 @@ __device__ __forceinline__ void decode_body(
   }
 
   __syncthreads();   // every ring has drained: the reduction reuses that LDS
-  float* sred = reinterpret_cast<float*>(smem);   // [waves][16][16 NT]
+  float* sred = reinterpret_cast<float*>(smem);   // [waves][16 rows][16 NT]
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sred[(wave * 16 + 4 * kq + i) * 16 * NT + 16 * t + col] = acc[t][i];
+    for (int i = 0; i < MR; ++i) sred[(wave * 16 + 4 * kq + i) * 16 * NT + 16 * t + col] = acc[t][i];
   __syncthreads();
-  const int outs = M * 16 * NT;
-  for (int idx = tid; idx < outs; idx += 64 * kDecWaves) {
-    const int m = idx / (16 * NT), c = idx % (16 * NT);
-    float s = 0.f;
+  // bf16 pairs of columns (c0, c1 and ldy even: 4-byte stores)
+  const int half = (c1 - c0) >> 1, pairs = M * half;
+  for (int idx = tid; idx < pairs; idx += 64 * kDecWaves) {
+    const int m = idx / half, c = c0 - n0 + 2 * (idx % half);
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) s += sred[(w * 16 + m) * 16 * NT + c];
-    y[static_cast<size_t>(m) * ldy + n0 + c] = static_cast<uint16_t>(f32_to_bf16(s));
+    for (int w = 0; w < kDecWaves; ++w) {
+      s0 += sred[(w * 16 + m) * 16 * NT + c];
+      s1 += sred[(w * 16 + m) * 16 * NT + c + 1];
+    }
+    *reinterpret_cast<uint32_t*>(y + static_cast<size_t>(m) * ldy + n0 + c) = f32_to_bf16(s0) | (f32_to_bf16(s1) << 16);
   }
 }
 
 template <bool kI8, bool kW5>
-__global__ __launch_bounds__(64 * kDecWaves, kDecPerCU) void gemm_decode_kernel(
+__global__ __launch_bounds__(64 * kDecWaves, 1) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ ASG, const float* __restrict__ RS,
     int M, int K, const u32x4* __restrict__ wpk, const uint32_t* __restrict__ hi,
     const uint32_t* __restrict__ sz, int N, DecodeMap map, uint16_t* __restrict__ y, int64_t ldy) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kDecLds];
-  const int b = blockIdx.x;
-  const int q = (b >= map.wg0[1]) + (b >= map.wg0[2]);          // partition
-  const int nwq = map.wg0[q + 1] - map.wg0[q], bq = b - map.wg0[q];
-  const int base = map.nt[q] / nwq, extra = map.nt[q] % nwq;
-  const int cnt = base + (bq < extra);
-  const int tfirst = map.t0[q] + bq * base + (bq < extra ? bq : extra);
+  const int b = blockIdx.x, W = map.wg0[3];
+  const int r = map.xcd ? (b % 8) * (W / 8) + b / 8 : b;
+  const int q = (r >= map.wg0[1]) + (r >= map.wg0[2]);          // partition
+  const int nwq = map.wg0[q + 1] - map.wg0[q], rq = r - map.wg0[q];
+  const int base = map.nq[q] / nwq, extra = map.nq[q] % nwq;
+  const int cnt = base + (rq < extra);
+  const int c0 = map.c0[q] + 4 * (rq * base + (rq < extra ? rq : extra));
+  const int c1 = c0 + 4 * cnt;
+  const int nt = ((c1 - 1) >> 4) - (c0 >> 4) + 1;
   const size_t MG = static_cast<size_t>(M) * (K >> 7);
   const float* asgp = ASG + q * MG;
   const float* rsp = RS + q * MG;
-#define PQ_DECODE_CASE(n)                                                                                     \
-  case n:                                                                                                     \
-    if constexpr (!kW5 || n <= kDecMaxNT5) {                                                                  \
-      if (M == 1) decode_body<n, 1, kI8, kW5>(A, asgp, rsp, M, K, wpk, hi, sz, N, q, tfirst, y, ldy, smem);   \
-      else decode_body<n, 4, kI8, kW5>(A, asgp, rsp, M, K, wpk, hi, sz, N, q, tfirst, y, ldy, smem);          \
-    }                                                                                                         \
+#define PQ_DECODE_CASE(n)                                                                                           \
+  case n:                                                                                                           \
+    if (M == 1) decode_body<n, 1, 8, kI8, kW5>(A, asgp, rsp, M, K, wpk, hi, sz, N, q, c0, c1, y, ldy, smem);         \
+    else if (M <= 8) decode_body<n, 4, 8, kI8, kW5>(A, asgp, rsp, M, K, wpk, hi, sz, N, q, c0, c1, y, ldy, smem);    \
+    else decode_body<n, 4, 16, kI8, kW5>(A, asgp, rsp, M, K, wpk, hi, sz, N, q, c0, c1, y, ldy, smem);               \
     break;
-  switch (cnt) {
+  switch (nt) {
     PQ_DECODE_CASE(1) PQ_DECODE_CASE(2) PQ_DECODE_CASE(3)
     PQ_DECODE_CASE(4) PQ_DECODE_CASE(5) PQ_DECODE_CASE(6)
     default: break;
@@ -501,31 +520,23 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecPerCU) void gemm_decode_kernel(
 #undef PQ_DECODE_CASE
 }
 
-// Deals the N/16 column tiles out to workgroups: a grid that is a multiple of the resident
-// workgroup slots (kDecPerCU per CU), each workgroup taking at most kDecMaxNT tiles per round,
-// split over the partitions in proportion to their tiles; returns the largest run of tiles any
-// workgroup gets.
-int decode_map(int N, int pb1, int pb2, int cus, int maxnt, DecodeMap* map) {
-  const int NTT = N / 16;
-  const int tb[4] = {0, pb1 < N ? pb1 / 16 : NTT, pb2 < N ? pb2 / 16 : NTT, NTT};
-  const int64_t slots = static_cast<int64_t>(kDecPerCU) * cus;
-  const int64_t rounds = (NTT + maxnt * slots - 1) / (maxnt * slots);
-  const int64_t W = std::min<int64_t>(NTT, rounds * slots);
-  int maxrun = 0, wg = 0;
+// Deals the N/4 column quarters out to ranges: about one range per CU (at most kDecMaxQ quarters
+// each, more ranges in rounds when N is that large), split over the partitions in proportion to
+// their quarters, each partition's quarters split evenly over its ranges.
+void decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
+  const int cb[4] = {0, pb1 < N ? pb1 : N, pb2 < N ? pb2 : N, N};
+  const int64_t Q = N / 4;
+  const int64_t tq = std::max<int64_t>(1, std::min<int64_t>(kDecMaxQ, (Q + cus - 1) / cus));
+  int wg = 0;
   for (int q = 0; q < 3; ++q) {
-    const int nt = tb[q + 1] - tb[q];
+    const int nq = (cb[q + 1] - cb[q]) / 4;
     map->wg0[q] = wg;
-    map->t0[q] = tb[q];
-    map->nt[q] = nt;
-    if (nt <= 0) continue;
-    int64_t w = (W * nt + NTT / 2) / NTT;
-    w = std::max<int64_t>(w, (nt + maxnt - 1) / maxnt);
-    w = std::min<int64_t>(std::max<int64_t>(w, 1), nt);
-    wg += static_cast<int>(w);
-    maxrun = std::max(maxrun, static_cast<int>((nt + w - 1) / w));
+    map->c0[q] = cb[q];
+    map->nq[q] = nq;
+    if (nq > 0) wg += static_cast<int>((nq + tq - 1) / tq);
   }
   map->wg0[3] = wg;
-  return maxrun;
+  map->xcd = (wg % 8) == 0;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1047,7 +1058,7 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
       asg = ex;
     }
     DecodeMap map;
-    decode_map(N, pb1, pb2, cu_count(), kW5 ? kDecMaxNT5 : kDecMaxNT, &map);
+    decode_map(N, pb1, pb2, cu_count(), &map);
     auto dec = gemm_decode_kernel<kI8, kW5>;
     hipLaunchKernelGGL(dec, dim3(map.wg0[3]), dim3(64 * kDecWaves), 0, s,
                        a_d, asg, rs_d, M, K, wpk, hi, sz, N, map, y_d, ldy);
