@@ -106,7 +106,8 @@ int pq_plan_partitions(int J, const int* ncols_h, const int16_t* const* pairs_h,
  *           codes reordered into matrix-core fragment order (1 KiB per 16 columns x 128-group,
  *           each 16-column strip's groups contiguous);
  *           then, per 16 columns, ceil(3*(K/128)/32) KiB of bf16 operands for the zero-point
- *           epilogue (the f32 values 8*sc + fl16(sc*(zp-8)) split into two bf16 pieces).
+ *           epilogue (the f32 values 8*sc + fl16(sc*(zp-8)) split into two bf16 pieces);
+ *           then (K/128) * N f32 column factors 512*sc for the prefill fold.
  *           Returns 0 for shapes the library rejects.
  * sz_d      out, f16 [K/128, N, 2]: {sc, fl16(sc * (zp - 8))} interleaved ("Design" item 1).
  * Requires K % 128 == 0, N % 16 == 0, 16-byte aligned wpk_d, 4-byte aligned others.
@@ -239,7 +240,8 @@ int pq_gemm_i8(const int8_t* a_d, const float* asg_d, const float* rs_d, int M, 
  *   wpk5_d    out, pq_packed_weight5_bytes(K, N) bytes: the K*N/2-byte nibble image of
  *             pq_pack_weights, then K*N/8 bytes of fifth bits in fragment order (256 bytes per
  *             16 columns x 128-group: lane l's 32-bit word carries the bits of its 32 codes),
- *             then the zero-point epilogue operand built from sc * (zp - 16).
+ *             then the zero-point epilogue operand built from sc * (zp - 16), then the f32 column
+ *             factors 512*sc as in pq_pack_weights.
  *   sz_d      out, f16 [K/128, N, 2]: {sc, fl16(sc * (zp - 16))}.
  *   Requires K % 128 == 0, N % 32 == 0, 16-byte aligned wpk5_d, 4-byte aligned others. Returns
  *   0 bytes from pq_packed_weight5_bytes for shapes the library rejects.

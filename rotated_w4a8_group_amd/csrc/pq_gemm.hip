@@ -14,7 +14,9 @@
 //     sc * sum_k D(a_k)(c_k - 8) - zsc * rs = (512 sc) * T - (8 sc + zsc) * rs,
 // both factors exact in fp32 (512 sc is a power-of-two scaling, 8 sc + zsc needs < 24 bits).
 //
-// Packed weight layout (pq_pack_weights), tile-major so that one column tile's whole K extent
+// Packed weight image (pq_pack_weights): the codes below, then the zero-point epilogue operand,
+// then the prefill fold's fp32 column factors 512 sc [G][N].
+// Packed code layout, tile-major so that one column tile's whole K extent
 // is one contiguous run: for 16-column tile t and group g, 1 KiB at ((t * G + g) * 1024): lane l (column 16t + l%16, k = 128g + 32*(l/16) + 0..31) owns 16 bytes
 // = 4 words; byte b of word q holds code(k0 + 8q + b) in its low nibble and code(k0 + 8q + 4 + b)
 // in its high nibble. (w & 0x0F0F0F0F) and ((w >> 4) & 0x0F0F0F0F) are then the lane's B
@@ -195,6 +197,13 @@ __global__ void pack_sz5_kernel(const int32_t* __restrict__ qzeros, const int32_
   const uint16_t sc = scales[idx];
   const _Float16 zsc = static_cast<_Float16>(f16_to_f32(sc) * static_cast<float>(zp - 16));
   sz[idx] = static_cast<uint32_t>(sc) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, zsc)) << 16);
+}
+
+// Column factors of the prefill kernel's fold, fp32 [G][N]: 512 sc from the SZ words (exact: a
+// power-of-two scaling of an f16 value), so the group loop reads them with no conversion.
+__global__ void pack_s9_kernel(const uint32_t* __restrict__ sz, int64_t gn, float* __restrict__ s9) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < gn) s9[i] = f16_to_f32(sz[i]) * 512.0f;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -568,12 +577,12 @@ struct PfTile {
   static constexpr int kOffA = 0;                              // [TM rows][8 chunks][16 B], chunks swizzled
   static constexpr int kOffB = TM * 128;                       // [TN/16 tiles][64 lanes][16 B]
   static constexpr int kOffAsg = kOffB + TN * 64;              // [TM] f32
-  static constexpr int kOffSz = kOffAsg + TM * 4;              // [TN] u32
-  static constexpr int kOffH = kOffSz + TN * 4;                // int5: [TN/16 tiles][64 lanes] u32
+  static constexpr int kOffS9 = kOffAsg + TM * 4;              // [TN] f32 column factors 512 sc
+  static constexpr int kOffH = kOffS9 + TN * 4;                // int5: [TN/16 tiles][64 lanes] u32
   static constexpr int kStage = (kOffH + (kW5 ? TN * 16 : 0) + 255) / 256 * 256;
-  static constexpr int nA = TM / 8, nB = TN / 16, nAs = kTok ? 0 : TM / 64, nSz = TN / 64;
+  static constexpr int nA = TM / 8, nB = TN / 16, nAs = kTok ? 0 : TM / 64, nS9 = TN / 64;
   static constexpr int nH = kW5 ? TN / 16 : 0;
-  static constexpr int nD = nA + nB + nAs + nSz + nH;          // direct loads per group
+  static constexpr int nD = nA + nB + nAs + nS9 + nH;          // direct loads per group
   static constexpr int kPerWave = (nD + 3) / 4;                 // loads per wave of the issuing half
   static constexpr int kOutStride = TN + 8;                    // bf16 per staged output row
   static_assert(WM * WN == kPfWaves && MF >= 1 && NF >= 1 && TM % 64 == 0 && TN % 64 == 0, "tile");
@@ -625,7 +634,7 @@ template <int TM, int TN, int WM, int WN, bool kTok, bool kI8, bool kW5, int S =
 __device__ __forceinline__ void prefill_tile(
     const uint8_t* __restrict__ A, const float* __restrict__ ASGT, int M, int K,
     const u32x4* __restrict__ wpk, const uint32_t* __restrict__ hi, const u32x4* __restrict__ zpe,
-    const u32x4* __restrict__ zpa, const uint32_t* __restrict__ sz, int N, int p, int m0, int n0,
+    const u32x4* __restrict__ zpa, const float* __restrict__ s9img, int N, int p, int m0, int n0,
     uint16_t* __restrict__ y, int64_t ldy, bool vec16, uint8_t* smem) {
   using TL = PfTile<TM, TN, WM, WN, kTok, kW5, S>;
   static_assert(S == 2 || S == 3, "the wait counts below cover rings of 2 and 3 stages");
@@ -635,7 +644,7 @@ __device__ __forceinline__ void prefill_tile(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: load table stays scalar
   const int wm = wave / WN, wn = wave % WN;
-  const int col = lane & 15, kq = lane >> 4;
+  const int kq = lane >> 4;
   const int last_tile = N / 16 - 1;
   const float* asgp = ASGT + static_cast<size_t>(p) * G * M;   // [G][M] for this partition
 
@@ -673,13 +682,13 @@ __device__ __forceinline__ void prefill_tile(
       sbase[i] = reinterpret_cast<const uint8_t*>(asgp);
       voff[i] = static_cast<uint32_t>(min(m0 + 64 * j + lane, M - 1) * 4);
       step[i] = static_cast<size_t>(M) * 4; dst[i] = TL::kOffAsg + j * 256; wide[i] = false;
-    } else if (d < TL::nA + TL::nB + TL::nAs + TL::nSz) {
+    } else if (d < TL::nA + TL::nB + TL::nAs + TL::nS9) {
       const int j = d - TL::nA - TL::nB - TL::nAs;
-      sbase[i] = reinterpret_cast<const uint8_t*>(sz);
+      sbase[i] = reinterpret_cast<const uint8_t*>(s9img);
       voff[i] = static_cast<uint32_t>(min(n0 + 64 * j + lane, N - 1) * 4);
-      step[i] = static_cast<size_t>(N) * 4; dst[i] = TL::kOffSz + j * 256; wide[i] = false;
+      step[i] = static_cast<size_t>(N) * 4; dst[i] = TL::kOffS9 + j * 256; wide[i] = false;
     } else {
-      const int j = d - TL::nA - TL::nB - TL::nAs - TL::nSz;   // int5 fifth-bit words of tile j
+      const int j = d - TL::nA - TL::nB - TL::nAs - TL::nS9;   // int5 fifth-bit words of tile j
       const int tt = min(n0 / 16 + j, last_tile);
       sbase[i] = reinterpret_cast<const uint8_t*>(hi) + static_cast<size_t>(tt) * G * 256;
       voff[i] = 4 * lane;
@@ -718,21 +727,23 @@ __device__ __forceinline__ void prefill_tile(
     if (g + D < G && (g & 1) == half) issue((g + D) % S, g + D);
     const uint8_t* st = smem + (g % S) * TL::kStage;
 
+    // Products are taken as (weights) x (activations)^T, so a lane's 4 results are one output row
+    // (the fragment row lane % 16) and 4 consecutive columns (4 (lane / 16) .. + 3): the row scale
+    // is one value per lane, the column factors a float4.
     v8i bf[NF];
-    float s9[NF];
+    float4 s9[NF];
 #pragma unroll
     for (int nf = 0; nf < NF; ++nf) {
       const uint32_t hw = kW5 ? *reinterpret_cast<const uint32_t*>(st + TL::kOffH + (wn * NF + nf) * 256 + lane * 4) : 0u;
       bf[nf] = weight_operand<kW5>(*reinterpret_cast<const u32x4*>(st + TL::kOffB + (wn * NF + nf) * 1024 + lane * 16), hw);
-      s9[nf] = f16_to_f32(*reinterpret_cast<const uint32_t*>(st + TL::kOffSz + (wn * NF * 16 + 16 * nf + col) * 4)) *
-               (kI8 ? 1.0f : 512.0f);   // e4m3 products carry 2^-9 per weight code
+      s9[nf] = *reinterpret_cast<const float4*>(st + TL::kOffS9 + (wn * NF * 16 + 16 * nf + 4 * kq) * 4);
     }
     // fragment lane l: row l%16 of the 16-row block, k chunks 2(l/16) and 2(l/16)+1, swizzled
     const int arow = lane & 15, ac0 = 2 * (lane >> 4), asw = (arow & 7) ^ (arow >> 3);
     const int aoff0 = arow * 128 + 16 * (ac0 ^ asw), aoff1 = arow * 128 + 16 * ((ac0 + 1) ^ asw);
     // the products of row fragment mf are issued before the fold of mf-1
     v4f Tb[2][NF];
-    float4 asb[2];
+    float asb[2];
 #pragma unroll
     for (int mf = 0; mf <= MF; ++mf) {
       if (mf < MF) {
@@ -740,27 +751,32 @@ __device__ __forceinline__ void prefill_tile(
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap + aoff0);
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + aoff1);
         const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        if constexpr (!kTok)
-          asb[mf & 1] = *reinterpret_cast<const float4*>(st + TL::kOffAsg + (wm * MF * 16 + 16 * mf + 4 * kq) * 4);
+        if constexpr (!kTok) {
+          asb[mf & 1] = *reinterpret_cast<const float*>(st + TL::kOffAsg + (wm * MF * 16 + 16 * mf + arow) * 4);
+          if constexpr (kI8) asb[mf & 1] *= 0x1p-9f;   // integer products carry no 2^-9 (exact)
+        }
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) Tb[mf & 1][nf] = group_product<kI8>(a, bf[nf]);
+        for (int nf = 0; nf < NF; ++nf) Tb[mf & 1][nf] = group_product<kI8>(bf[nf], a);
       }
       if (mf > 0) {
         const int pm = mf - 1;
         if constexpr (kTok) {
           // per-token scales: the row scale is applied once in the epilogue
 #pragma unroll
-          for (int nf = 0; nf < NF; ++nf)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[pm][nf][i] = __builtin_fmaf(s9[nf], Tb[pm & 1][nf][i], acc[pm][nf][i]);
+          for (int nf = 0; nf < NF; ++nf) {
+            acc[pm][nf][0] = __builtin_fmaf(s9[nf].x, Tb[pm & 1][nf][0], acc[pm][nf][0]);
+            acc[pm][nf][1] = __builtin_fmaf(s9[nf].y, Tb[pm & 1][nf][1], acc[pm][nf][1]);
+            acc[pm][nf][2] = __builtin_fmaf(s9[nf].z, Tb[pm & 1][nf][2], acc[pm][nf][2]);
+            acc[pm][nf][3] = __builtin_fmaf(s9[nf].w, Tb[pm & 1][nf][3], acc[pm][nf][3]);
+          }
         } else {
-          const float4 as = asb[pm & 1];
+          const float as = asb[pm & 1];
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf) {
-            acc[pm][nf][0] = __builtin_fmaf(as.x * s9[nf], Tb[pm & 1][nf][0], acc[pm][nf][0]);
-            acc[pm][nf][1] = __builtin_fmaf(as.y * s9[nf], Tb[pm & 1][nf][1], acc[pm][nf][1]);
-            acc[pm][nf][2] = __builtin_fmaf(as.z * s9[nf], Tb[pm & 1][nf][2], acc[pm][nf][2]);
-            acc[pm][nf][3] = __builtin_fmaf(as.w * s9[nf], Tb[pm & 1][nf][3], acc[pm][nf][3]);
+            acc[pm][nf][0] = __builtin_fmaf(as * s9[nf].x, Tb[pm & 1][nf][0], acc[pm][nf][0]);
+            acc[pm][nf][1] = __builtin_fmaf(as * s9[nf].y, Tb[pm & 1][nf][1], acc[pm][nf][1]);
+            acc[pm][nf][2] = __builtin_fmaf(as * s9[nf].z, Tb[pm & 1][nf][2], acc[pm][nf][2]);
+            acc[pm][nf][3] = __builtin_fmaf(as * s9[nf].w, Tb[pm & 1][nf][3], acc[pm][nf][3]);
           }
         }
       }
@@ -811,36 +827,30 @@ __device__ __forceinline__ void prefill_tile(
           const u32x4 za = *reinterpret_cast<const u32x4*>(zb0 + ((wm * MF + mf) * ZC + j) * 1024);
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf)
-            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za),
-                                                                   __builtin_bit_cast(bf16x8, zb[nf]), acc[mf][nf], 0, 0, 0);
+            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, zb[nf]),
+                                                                   __builtin_bit_cast(bf16x8, za), acc[mf][nf], 0, 0, 0);
         }
       }
     }
   }
 
-  if constexpr (kTok) {
-    // per-token scale of each row (ASGT holds AS [P][M] in this mode)
-#pragma unroll
-    for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = min(m0 + wm * MF * 16 + 16 * mf + 4 * kq + i, M - 1);
-        const float a = ASGT[static_cast<size_t>(p) * M + row];
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf) acc[mf][nf][i] *= a;
-      }
-  }
   // ---- bf16 tile through LDS (the ring is idle now), then whole rows with wide stores
   __syncthreads();   // every wave has finished reading the ring
+  // (per-token path: each row's token scale is applied here; ASGT holds AS [P][M] in that mode and
+  // the lane's row is lane % 16 of the fragment)
   uint16_t* ot = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-  for (int mf = 0; mf < MF; ++mf)
+  for (int mf = 0; mf < MF; ++mf) {
+    float a = 1.0f;
+    if constexpr (kTok) a = ASGT[static_cast<size_t>(p) * M + min(m0 + wm * MF * 16 + 16 * mf + (lane & 15), M - 1)];
 #pragma unroll
-    for (int nf = 0; nf < NF; ++nf)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ot[(wm * MF * 16 + 16 * mf + 4 * kq + i) * TL::kOutStride + wn * NF * 16 + 16 * nf + col] =
-            static_cast<uint16_t>(f32_to_bf16(acc[mf][nf][i]));
+    for (int nf = 0; nf < NF; ++nf) {
+      v4f v = acc[mf][nf];
+      if constexpr (kTok) v *= a;
+      *reinterpret_cast<uint2*>(ot + (wm * MF * 16 + 16 * mf + (lane & 15)) * TL::kOutStride + wn * NF * 16 + 16 * nf + 4 * kq) =
+          make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
+    }
+  }
   __syncthreads();
   store_tile_rows<TM, TN, TL::kOutStride>(ot, y, ldy, m0, n0, M, N, vec16);
 }
@@ -861,7 +871,7 @@ template <bool kTok, bool kI8, bool kW5>
 __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ ASGT, int M, int K,
     const u32x4* __restrict__ wpk, const uint32_t* __restrict__ hi, const u32x4* __restrict__ zpe,
-    const u32x4* __restrict__ zpa, const uint32_t* __restrict__ sz, int N, int pb1, int pb2,
+    const u32x4* __restrict__ zpa, const float* __restrict__ s9img, int N, int pb1, int pb2,
     uint16_t* __restrict__ y, int64_t ldy, PrefillMap map, bool vec16) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfLds];
   const int b = blockIdx.x;
@@ -881,22 +891,22 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
   if constexpr (kW5) {
     if (map.shape == kPfWide) {
       // the fifth-bit planes make a 256x256 stage 54 KiB: a ring of two (one group loaded ahead)
-      if (split == 1) prefill_tile<256, 256, 2, 4, kTok, kI8, true, 2>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-      else if (split == 2) prefill_tile<128, 256, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-      else if (split == 4) prefill_tile<128, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-      else prefill_tile<64, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+      if (split == 1) prefill_tile<256, 256, 2, 4, kTok, kI8, true, 2>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
+      else if (split == 2) prefill_tile<128, 256, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
+      else if (split == 4) prefill_tile<128, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
+      else prefill_tile<64, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
       return;
     }
-    if (split == 1) prefill_tile<128, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (split == 1) prefill_tile<128, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4, kTok, kI8, true>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
   } else if (map.shape == kPfWide) {
-    if (split == 1) prefill_tile<256, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else if (split == 2) prefill_tile<128, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else if (split == 4) prefill_tile<128, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (split == 1) prefill_tile<256, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 2) prefill_tile<128, 256, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
+    else if (split == 4) prefill_tile<128, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
   } else {
-    if (split == 1) prefill_tile<128, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
-    else prefill_tile<64, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, sz, N, p, m0, n0, y, ldy, vec16, smem);
+    if (split == 1) prefill_tile<128, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
+    else prefill_tile<64, 128, 2, 4, kTok, kI8, false>(A, ASGT, M, K, wpk, hi, zpe, zpa, s9img, N, p, m0, n0, y, ldy, vec16, smem);
   }
 }
 
@@ -946,7 +956,7 @@ size_t pq_packed_weight_bytes(int K, int N) {
   if (K <= 0 || N <= 0 || K % PQ_GROUP || N % 16) return 0;
   const size_t codes = static_cast<size_t>(K) * static_cast<size_t>(N) / 2;
   const size_t zpe = static_cast<size_t>(N / 16) * pq::zpe_chunks(K / PQ_GROUP) * 1024;
-  return codes + zpe;
+  return codes + zpe + static_cast<size_t>(K / PQ_GROUP) * N * 4;
 }
 
 int pq_pack_weights(const int32_t* qweight_d, const int32_t* qzeros_d, const uint16_t* scales_d,
@@ -971,6 +981,9 @@ int pq_pack_weights(const int32_t* qweight_d, const int32_t* qzeros_d, const uin
   auto zk = pack_zpe_kernel<false>;
   hipLaunchKernelGGL(zk, dim3(static_cast<unsigned>((zl + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t*>(sz_d), G, N, zpe);
+  float* s9 = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(zpe) + static_cast<size_t>(N / 16) * zpe_chunks(G) * 1024);
+  hipLaunchKernelGGL(pack_s9_kernel, dim3(static_cast<unsigned>((gn + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(sz_d), gn, s9);
   return launch_status("pq_pack_weights");
 }
 
@@ -978,7 +991,7 @@ size_t pq_packed_weight5_bytes(int K, int N) {
   if (K <= 0 || N <= 0 || K % PQ_GROUP || N % 32) return 0;
   const size_t kn = static_cast<size_t>(K) * static_cast<size_t>(N);
   const size_t zpe = static_cast<size_t>(N / 16) * pq::zpe_chunks(K / PQ_GROUP) * 1024;
-  return kn / 2 + kn / 8 + zpe;
+  return kn / 2 + kn / 8 + zpe + static_cast<size_t>(K / PQ_GROUP) * N * 4;
 }
 
 int pq_pack_weights5(const int32_t* qweight_d, const int32_t* qweight_hi_d, const int32_t* qzeros_d,
@@ -1010,6 +1023,9 @@ int pq_pack_weights5(const int32_t* qweight_d, const int32_t* qweight_hi_d, cons
   auto zk = pack_zpe_kernel<true>;
   hipLaunchKernelGGL(zk, dim3(static_cast<unsigned>((zl + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t*>(sz_d), G, N, zpe);
+  float* s9 = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(zpe) + static_cast<size_t>(N / 16) * zpe_chunks(G) * 1024);
+  hipLaunchKernelGGL(pack_s9_kernel, dim3(static_cast<unsigned>((gn + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(sz_d), gn, s9);
   return launch_status("pq_pack_weights5");
 }
 
@@ -1047,6 +1063,8 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
   const uint8_t* wb = static_cast<const uint8_t*>(wpk_d);
   const uint32_t* hi = kW5 ? reinterpret_cast<const uint32_t*>(wb + static_cast<size_t>(K) * N / 2) : nullptr;
   const u32x4* zpe = reinterpret_cast<const u32x4*>(wb + static_cast<size_t>(K) * N / 2 + (kW5 ? static_cast<size_t>(K) * N / 8 : 0));
+  const float* s9img = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(zpe) +
+                                                      static_cast<size_t>(N / 16) * zpe_chunks(G) * 1024);
   if (M <= 16) {
     const float* asg = a_scale;
     if (kTok) {
@@ -1085,7 +1103,7 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
   const bool vec16 = aligned(y_d, 16) && ldy % 8 == 0;
   auto prefill = gemm_prefill_kernel<kTok, kI8, kW5>;
   hipLaunchKernelGGL(prefill, dim3(static_cast<unsigned>(grid)), dim3(64 * kPfWaves), 0, s,
-                     a_d, kTok ? a_scale : asgt, M, K, wpk, hi, zpe, zpa, sz, N, pb1, pb2, y_d, ldy, map, vec16);
+                     a_d, kTok ? a_scale : asgt, M, K, wpk, hi, zpe, zpa, s9img, N, pb1, pb2, y_d, ldy, map, vec16);
   return launch_status(what);
 }
 

@@ -220,7 +220,7 @@ def test_gemm5_and_pack5_validation():
     assert lib.pq_pack_weights5(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 64, FAKE, FAKE, None) == -2
     assert lib.pq_pack_weights5(FAKE, None, FAKE, FAKE, FAKE, 256, 64, FAKE, FAKE, None) == -1
     # nibble image + fifth-bit planes (K N / 8) + zero-point operand
-    assert lib.pq_packed_weight5_bytes(5120, 17408) == 5120 * 17408 // 2 + 5120 * 17408 // 8 + 1088 * 4 * 1024
+    assert lib.pq_packed_weight5_bytes(5120, 17408) == 5120 * 17408 // 2 + 5120 * 17408 // 8 + 1088 * 4 * 1024 + 40 * 17408 * 4
     assert lib.pq_packed_weight5_bytes(256, 48) == 0
 
 
@@ -275,7 +275,8 @@ def test_pack_validation():
     assert L.pq_pack_weights(None, FAKE, FAKE, 256, 128, FAKE, FAKE, None) == -1
     assert L.pq_pack_weights(FAKE, FAKE, FAKE, 256, 128, ctypes.c_void_p(0x100008), FAKE, None) == -3
     # codes (K*N/2) + the zero-point epilogue operand: N/16 tiles x ceil(3G/32) chunks x 1 KiB
-    assert L.pq_packed_weight_bytes(5120, 17408) == 5120 * 17408 // 2 + (17408 // 16) * 4 * 1024
+    # + the fp32 column factors of the prefill fold (G x N x 4 bytes)
+    assert L.pq_packed_weight_bytes(5120, 17408) == 5120 * 17408 // 2 + (17408 // 16) * 4 * 1024 + 40 * 17408 * 4
     assert L.pq_packed_weight_bytes(17408, 5120) == 17408 * 5120 // 2 + (5120 // 16) * 13 * 1024
     assert L.pq_packed_weight_bytes(100, 16) == 0
 
