@@ -277,7 +277,7 @@ def test_pack_validation():
     # codes (K*N/2) + the zero-point epilogue operand: N/16 tiles x ceil(3G/32) chunks x 1 KiB
     # + the fp32 column factors of the prefill fold (G x N x 4 bytes)
     assert L.pq_packed_weight_bytes(5120, 17408) == 5120 * 17408 // 2 + (17408 // 16) * 4 * 1024 + 40 * 17408 * 4
-    assert L.pq_packed_weight_bytes(17408, 5120) == 17408 * 5120 // 2 + (5120 // 16) * 13 * 1024
+    assert L.pq_packed_weight_bytes(17408, 5120) == 17408 * 5120 // 2 + (5120 // 16) * 13 * 1024 + 136 * 5120 * 4
     assert L.pq_packed_weight_bytes(100, 16) == 0
 
 
