@@ -557,11 +557,11 @@ void decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
 // index XOR-swizzled by (row%8) ^ ((row/8)%2): each 16-lane quarter of a fragment read then
 // covers the 64 LDS banks once (measured on gfx950: (row/2)%8 and row%8 read ~40% slower); the
 // weight image is already in fragment order (each lane reads 16 contiguous bytes). Per group and wave the
-// products T = MFMA(A_g, codes_g) are folded as acc += (asg * 512 sc) * T (2 VALU per output),
-// each row fragment's products issued before the previous fragment's fold. After the loop the
-// zero-point term is subtracted as a bf16 matrix-core product (pack_zpe_kernel / zpe_act_kernel
-// operands, staged through the idle ring), and the bf16 tile is staged in LDS and written as
-// whole rows.
+// products T = MFMA(codes_g, A_g) are folded as acc += (asg * 512 sc) * T (2 VALU per output),
+// each row fragment's products issued before the previous fragment's fold. The zero-point term is
+// subtracted as a bf16 matrix-core product (pack_zpe_kernel / zpe_act_kernel operands) in KC more
+// k-steps of the same ring, their loads issued while the last groups compute; the bf16 tile is then
+// staged in LDS and written as whole rows.
 //
 // Tiles (PrefillMap): whole rounds of 256x256 tiles, one workgroup per CU; the tiles of the
 // last, partial round are cut into 2, 4 or 8 pieces (128x256, 128x128, 64x128) so that round
@@ -704,6 +704,32 @@ __device__ __forceinline__ void prefill_tile(
       else lds_dma4_s(sbase[i] + g * step[i], voff[i], st + dst[i]);
     }
   };
+  // Zero-point epilogue operands (pack_zpe_kernel / zpe_act_kernel): for chunk c of KC, the tile's
+  // TM/16 activation-side and TN/16 weight-side fragments, 1 KiB each, go to a stage at
+  // f * 1024 (f = fragment) like one more group; this half's share: fragments (wave % 4) + 4 i.
+  // The source of each is computed on the scalar unit when it is issued.
+  constexpr int NZ = TM / 16 + TN / 16, PWZ = (NZ + 3) / 4;
+  static_assert(PWZ <= PW && NZ * 1024 <= TL::kStage, "zero-point chunks ride the group ring");
+  const int KC = zpe_chunks(G), MT = (M + 15) / 16;
+  auto zissue = [&](int stage, int c) {
+    const uint32_t st = lds0 + stage * TL::kStage;
+#pragma unroll
+    for (int i = 0; i < PWZ; ++i) {
+      const int f = (wave & 3) + 4 * i;
+      if (f < NZ) {
+        const uint8_t* src = (f < TM / 16)
+            ? reinterpret_cast<const uint8_t*>(zpa) + ((static_cast<size_t>(p) * MT + min(m0 / 16 + f, MT - 1)) * KC + c) * 1024
+            : reinterpret_cast<const uint8_t*>(zpe) + (static_cast<size_t>(min(n0 / 16 + f - TM / 16, last_tile)) * KC + c) * 1024;
+        lds_dma16_s(src, 16 * lane, st + f * 1024);
+      }
+    }
+  };
+  // k-steps 0 .. G-1 are the groups, G .. G+KC-1 the zero-point chunks
+  const int GT = G + KC;
+  auto issue_step = [&](int stage, int j) {
+    if (j < G) issue(stage, j);
+    else zissue(stage, j - G);
+  };
 
   v4f acc[MF][NF];
 #pragma unroll
@@ -714,17 +740,21 @@ __device__ __forceinline__ void prefill_tile(
   // Group j's loads go into stage j % S and are issued during group j - D (D = S - 1 groups
   // ahead; the first D groups before the loop) by half (j - D) % 2.
   const int half = wave >> 2;
-  for (int j = 0; j < D && j < G; ++j)
-    if (((j - D) & 1) == half) issue(j % S, j);
-  for (int g = 0; g < G; ++g) {
-    // Group g was loaded by half (g - D) % 2, whose only outstanding loads are group g's: it
-    // waits for all of them. With D = 2 the other half's outstanding loads (at most PW, group
-    // g+1) need not land; with D = 1 it has none. The barrier then makes group g visible to every
-    // wave and guarantees that no wave still reads stage (g + D) % S, the one group g - 1 used.
-    // (__syncthreads would also drain the group g+1 loads.)
+  for (int j = 0; j < D && j < GT; ++j)
+    if (((j - D) & 1) == half) issue_step(j % S, j);
+  // Step g was loaded by half (g - D) % 2, whose only outstanding loads are step g's: it waits
+  // for all of them. With D = 2 the other half's outstanding loads (at most PW, step g+1) need
+  // not land; with D = 1 it has none. The barrier then makes step g visible to every wave and
+  // guarantees that no wave still reads stage (g + D) % S, the one step g - 1 used.
+  // (__syncthreads would also drain the step g+1 loads.) A zero-point chunk step has at most
+  // PWZ <= PW loads per wave, so the same waits hold.
+  auto step_begin = [&](int g) {
     if (((g - D) & 1) == half) wait_vm_lgkm_barrier<0>();
     else wait_vm_lgkm_barrier<D >= 2 ? PW : 0>();
-    if (g + D < G && (g & 1) == half) issue((g + D) % S, g + D);
+    if (g + D < GT && (g & 1) == half) issue_step((g + D) % S, g + D);
+  };
+  for (int g = 0; g < G; ++g) {
+    step_begin(g);
     const uint8_t* st = smem + (g % S) * TL::kStage;
 
     // Products are taken as (weights) x (activations)^T, so a lane's 4 results are one output row
@@ -782,55 +812,22 @@ __device__ __forceinline__ void prefill_tile(
       }
     }
   }
-
-  // ---- zero-point epilogue: acc += (-[a1|a1|a2]) x [z1;z2;z1] over KC chunks of 32 k'. The
-  // tile's operands (TM/16 row and TN/16 column fragments, 1 KiB per fragment and chunk) move to
-  // LDS by direct loads, ZC chunks per batch into two alternating buffers of the idle ring, so
-  // each byte crosses the load path once per workgroup.
-  {
-    constexpr int ZC = 2;
-    constexpr int NZ = TM / 16 + TN / 16;
-    constexpr int kZBuf = NZ * ZC * 1024;
-    constexpr int ZPW = (NZ * ZC + kPfWaves - 1) / kPfWaves;
-    static_assert(2 * kZBuf <= kPfLds, "LDS");
-    const int KC = zpe_chunks(G), MT = (M + 15) / 16;
-    const uint8_t* zab = reinterpret_cast<const uint8_t*>(zpa) + static_cast<size_t>(p) * MT * KC * 1024;
-    const uint8_t* zwb = reinterpret_cast<const uint8_t*>(zpe);
-    auto zissue = [&](int buf, int c0) {
+  // zero-point chunk c = g - G: acc += (-[a1|a1|a2]) x [z1;z2;z1] over its 32 k' (bf16 pieces of
+  // asg*rs and of the zero-point factor, relative error ~2^-16), weights as the first operand
+  for (int g = G; g < GT; ++g) {
+    step_begin(g);
+    const uint8_t* st = smem + (g % S) * TL::kStage;
+    u32x4 zb[NF];
 #pragma unroll
-      for (int i = 0; i < ZPW; ++i) {
-        const int d = wave + kPfWaves * i;                 // entry d: fragment d / ZC, chunk d % ZC
-        if (d < NZ * ZC) {
-          const int f = d / ZC, c = min(c0 + d % ZC, KC - 1);
-          const uint8_t* src = (f < TM / 16)
-              ? zab + (static_cast<size_t>(min(m0 / 16 + f, MT - 1)) * KC + c) * 1024
-              : zwb + (static_cast<size_t>(min(n0 / 16 + f - TM / 16, last_tile)) * KC + c) * 1024;
-          lds_dma16(src + lane * 16, lds0 + buf * kZBuf + d * 1024);
-        }
-      }
-    };
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the ring is idle
-    zissue(0, 0);
-    for (int c0 = 0, buf = 0; c0 < KC; c0 += ZC, buf ^= 1) {
-      wait_vm_lgkm_barrier<0>();        // batch c0 visible; every wave is done with buffer buf^1
-      if (c0 + ZC < KC) zissue(buf ^ 1, c0 + ZC);
-      const uint8_t* zb0 = smem + buf * kZBuf + lane * 16;
+    for (int nf = 0; nf < NF; ++nf)
+      zb[nf] = *reinterpret_cast<const u32x4*>(st + (TM / 16 + wn * NF + nf) * 1024 + lane * 16);
 #pragma unroll
-      for (int j = 0; j < ZC; ++j) {
-        if (c0 + j >= KC) break;
-        u32x4 zb[NF];
+    for (int mf = 0; mf < MF; ++mf) {
+      const u32x4 za = *reinterpret_cast<const u32x4*>(st + (wm * MF + mf) * 1024 + lane * 16);
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf)
-          zb[nf] = *reinterpret_cast<const u32x4*>(zb0 + ((TM / 16 + wn * NF + nf) * ZC + j) * 1024);
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf) {
-          const u32x4 za = *reinterpret_cast<const u32x4*>(zb0 + ((wm * MF + mf) * ZC + j) * 1024);
-#pragma unroll
-          for (int nf = 0; nf < NF; ++nf)
-            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, zb[nf]),
-                                                                   __builtin_bit_cast(bf16x8, za), acc[mf][nf], 0, 0, 0);
-        }
-      }
+      for (int nf = 0; nf < NF; ++nf)
+        acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, zb[nf]),
+                                                               __builtin_bit_cast(bf16x8, za), acc[mf][nf], 0, 0, 0);
     }
   }
 
