@@ -760,55 +760,61 @@ __device__ __forceinline__ void prefill_tile(
     // Products are taken as (weights) x (activations)^T, so a lane's 4 results are one output row
     // (the fragment row lane % 16) and 4 consecutive columns (4 (lane / 16) .. + 3): the row scale
     // is one value per lane, the column factors a float4.
+    u32x4 braw[NF];
+    uint32_t hw[NF];
     v8i bf[NF];
     float4 s9[NF];
 #pragma unroll
     for (int nf = 0; nf < NF; ++nf) {
-      const uint32_t hw = kW5 ? *reinterpret_cast<const uint32_t*>(st + TL::kOffH + (wn * NF + nf) * 256 + lane * 4) : 0u;
-      bf[nf] = weight_operand<kW5>(*reinterpret_cast<const u32x4*>(st + TL::kOffB + (wn * NF + nf) * 1024 + lane * 16), hw);
+      hw[nf] = kW5 ? *reinterpret_cast<const uint32_t*>(st + TL::kOffH + (wn * NF + nf) * 256 + lane * 4) : 0u;
+      braw[nf] = *reinterpret_cast<const u32x4*>(st + TL::kOffB + (wn * NF + nf) * 1024 + lane * 16);
       s9[nf] = *reinterpret_cast<const float4*>(st + TL::kOffS9 + (wn * NF * 16 + 16 * nf + 4 * kq) * 4);
     }
     // fragment lane l: row l%16 of the 16-row block, k chunks 2(l/16) and 2(l/16)+1, swizzled
     const int arow = lane & 15, ac0 = 2 * (lane >> 4), asw = (arow & 7) ^ (arow >> 3);
     const int aoff0 = arow * 128 + 16 * (ac0 ^ asw), aoff1 = arow * 128 + 16 * ((ac0 + 1) ^ asw);
-    // the products of row fragment mf are issued before the fold of mf-1
+    auto load_a = [&](int mf, v8i& a, float& as) {
+      const uint8_t* ap = st + TL::kOffA + (wm * MF + mf) * 2048;
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap + aoff0);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + aoff1);
+      a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      if constexpr (!kTok) as = *reinterpret_cast<const float*>(st + TL::kOffAsg + (wm * MF * 16 + 16 * mf + arow) * 4);
+    };
+    // Row fragment mf's products are interleaved one for one with the folds of fragment mf-1
+    // (acc += f T, f = asg * 512 sc: 8 VALU per product), so the matrix core and the vector ALU
+    // work side by side; fragment mf+1's operands are read from LDS while mf computes, and the
+    // weight codes are unpacked beside fragment 0's products.
     v4f Tb[2][NF];
-    float asb[2];
+    v8i a[2];
+    float asb[2] = {0.f, 0.f};
+    load_a(0, a[0], asb[0]);
 #pragma unroll
     for (int mf = 0; mf <= MF; ++mf) {
-      if (mf < MF) {
-        const uint8_t* ap = st + TL::kOffA + (wm * MF + mf) * 2048;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap + aoff0);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + aoff1);
-        const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        if constexpr (!kTok) {
-          asb[mf & 1] = *reinterpret_cast<const float*>(st + TL::kOffAsg + (wm * MF * 16 + 16 * mf + arow) * 4);
-          if constexpr (kI8) asb[mf & 1] *= 0x1p-9f;   // integer products carry no 2^-9 (exact)
-        }
+      // fragment mf-1's row scale is taken before the prefetch reuses its slot
+      const int pm = mf - 1;
+      float as = 0.f;
+      if constexpr (!kTok) as = kI8 ? asb[pm & 1] * 0x1p-9f : asb[pm & 1];   // integer products carry no 2^-9
+      if (mf + 1 < MF) load_a(mf + 1, a[(mf + 1) & 1], asb[(mf + 1) & 1]);
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) Tb[mf & 1][nf] = group_product<kI8>(bf[nf], a);
-      }
-      if (mf > 0) {
-        const int pm = mf - 1;
-        if constexpr (kTok) {
-          // per-token scales: the row scale is applied once in the epilogue
-#pragma unroll
-          for (int nf = 0; nf < NF; ++nf) {
-            acc[pm][nf][0] = __builtin_fmaf(s9[nf].x, Tb[pm & 1][nf][0], acc[pm][nf][0]);
-            acc[pm][nf][1] = __builtin_fmaf(s9[nf].y, Tb[pm & 1][nf][1], acc[pm][nf][1]);
-            acc[pm][nf][2] = __builtin_fmaf(s9[nf].z, Tb[pm & 1][nf][2], acc[pm][nf][2]);
-            acc[pm][nf][3] = __builtin_fmaf(s9[nf].w, Tb[pm & 1][nf][3], acc[pm][nf][3]);
-          }
-        } else {
-          const float as = asb[pm & 1];
-#pragma unroll
-          for (int nf = 0; nf < NF; ++nf) {
-            acc[pm][nf][0] = __builtin_fmaf(as * s9[nf].x, Tb[pm & 1][nf][0], acc[pm][nf][0]);
-            acc[pm][nf][1] = __builtin_fmaf(as * s9[nf].y, Tb[pm & 1][nf][1], acc[pm][nf][1]);
-            acc[pm][nf][2] = __builtin_fmaf(as * s9[nf].z, Tb[pm & 1][nf][2], acc[pm][nf][2]);
-            acc[pm][nf][3] = __builtin_fmaf(as * s9[nf].w, Tb[pm & 1][nf][3], acc[pm][nf][3]);
+      for (int nf = 0; nf < NF; ++nf) {
+        if (mf == 0) bf[nf] = weight_operand<kW5>(braw[nf], hw[nf]);
+        if (mf < MF) Tb[mf & 1][nf] = group_product<kI8>(bf[nf], a[mf & 1]);
+        if (mf > 0) {
+          const v4f& T = Tb[pm & 1][nf];
+          if constexpr (kTok) {
+            // per-token scales: the row scale is applied once in the epilogue
+            acc[pm][nf][0] = __builtin_fmaf(s9[nf].x, T[0], acc[pm][nf][0]);
+            acc[pm][nf][1] = __builtin_fmaf(s9[nf].y, T[1], acc[pm][nf][1]);
+            acc[pm][nf][2] = __builtin_fmaf(s9[nf].z, T[2], acc[pm][nf][2]);
+            acc[pm][nf][3] = __builtin_fmaf(s9[nf].w, T[3], acc[pm][nf][3]);
+          } else {
+            acc[pm][nf][0] = __builtin_fmaf(as * s9[nf].x, T[0], acc[pm][nf][0]);
+            acc[pm][nf][1] = __builtin_fmaf(as * s9[nf].y, T[1], acc[pm][nf][1]);
+            acc[pm][nf][2] = __builtin_fmaf(as * s9[nf].z, T[2], acc[pm][nf][2]);
+            acc[pm][nf][3] = __builtin_fmaf(as * s9[nf].w, T[3], acc[pm][nf][3]);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
