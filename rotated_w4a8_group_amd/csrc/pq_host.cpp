@@ -86,7 +86,8 @@ static double f16_to_double(uint16_t h) {
   return s ? -v : v;
 }
 
-// Lane order for the 64 pairs of one (layer, group).
+// Lane order for the 64 pairs of the first layer of a group (later layers follow from it, see
+// chain_group).
 //
 // The prologue keeps 4 tokens of a token-group in LDS token-minor: channel c occupies the
 // 16-byte row lds_row(c) = c + c/8 (one padding row per 8 channels). In each layer lane l reads
@@ -198,6 +199,114 @@ static bool order_layer(const int* pi, const int* pj, int* tail, int* head, int*
   return true;
 }
 
+// Proper edge colouring of a bipartite multigraph in which every node has degree deg: n left
+// and n right nodes, edge e joins left[e] and right[e]. Colour c's edges form a perfect matching
+// (found by augmenting paths among the uncoloured edges; a regular bipartite multigraph always
+// has one, and removing it leaves a regular one). Returns false only if that fails.
+static bool colour_regular(int n, int deg, const int* left, const int* right, int* colour) {
+  const int E = n * deg;
+  for (int e = 0; e < E; ++e) colour[e] = -1;
+  for (int c = 0; c < deg; ++c) {
+    std::vector<int> match_r(n, -1), match_l(n, -1);   // node -> edge
+    for (int u = 0; u < n; ++u) {
+      std::vector<int> prev_edge(n, -1);
+      std::vector<bool> seen(n, false);
+      std::vector<int> queue{u};
+      int found = -1;
+      for (size_t qi = 0; qi < queue.size() && found < 0; ++qi) {
+        const int a = queue[qi];
+        for (int e = 0; e < E && found < 0; ++e) {
+          if (colour[e] >= 0 || left[e] != a || seen[right[e]]) continue;
+          seen[right[e]] = true;
+          prev_edge[right[e]] = e;
+          if (match_r[right[e]] < 0) found = right[e];
+          else queue.push_back(left[match_r[right[e]]]);
+        }
+      }
+      if (found < 0) return false;
+      for (int b = found; b >= 0;) {
+        const int e = prev_edge[b];
+        const int a = left[e];
+        const int next = match_l[a] >= 0 ? right[match_l[a]] : -1;
+        match_r[b] = e;
+        match_l[a] = e;
+        b = (a == u) ? -1 : next;
+      }
+    }
+    for (int a = 0; a < n; ++a) colour[match_l[a]] = c;
+  }
+  return true;
+}
+
+// The record chain of one group (8 layers x 64 lanes), see pq_build_records: pi[r][q], pj[r][q]
+// are the channels of pair q of layer r. Layer 0 takes order_layer's lanes. From each layer to
+// the next, the two pairings form even cycles; keeping alternate channels along each cycle gives
+// every lane one output it consumes itself in the next layer (that layer's first operand) and one
+// it hands to another lane through an LDS row, chosen so that both the writes and the reads are
+// free of bank conflicts. Returns false only on an internal failure.
+struct LaneRec {
+  int u, v;          // the lane's pair as it computes it: u the first operand, v the second
+  int rslot, wslot;  // hand-off rows read (layers 1..7) and written (layers 0..6)
+  bool keep_v;       // the output kept in registers for the next layer is v's (layers 0..6)
+};
+static bool chain_group(const int (*pi)[64], const int (*pj)[64], LaneRec (*out)[64]) {
+  // layer 0: lane order and orientation from order_layer (conflict-free reads of the image)
+  {
+    int tail[64], head[64], lane_of[64];
+    if (!order_layer(pi[0], pj[0], tail, head, lane_of)) return false;
+    for (int q = 0; q < 64; ++q) out[0][lane_of[q]] = LaneRec{tail[q], head[q], 0, 0, false};
+  }
+  for (int r = 0; r + 1 < PQ_LAYERS; ++r) {
+    int nxt[128], lane_at[128];
+    for (int q = 0; q < 64; ++q) { nxt[pi[r + 1][q]] = pj[r + 1][q]; nxt[pj[r + 1][q]] = pi[r + 1][q]; }
+    for (int l = 0; l < 64; ++l) { lane_at[out[r][l].u] = l; lane_at[out[r][l].v] = l; }
+    // Along each cycle of layer r's and layer r+1's pairings, keep alternate ends: every pair of
+    // layer r then keeps one channel and every pair of layer r+1 contains exactly one kept one.
+    int keep[64];
+    bool done[64] = {false};
+    for (int l0 = 0; l0 < 64; ++l0) {
+      if (done[l0]) continue;
+      int l = l0, k = out[r][l0].u;
+      while (true) {
+        done[l] = true;
+        keep[l] = k;
+        const int x = nxt[k];             // handed off by its layer-r lane
+        const int lx = lane_at[x];
+        if (lx == l0) {
+          if (x != (out[r][l0].u == keep[l0] ? out[r][l0].v : out[r][l0].u)) return false;
+          break;
+        }
+        if (done[lx]) return false;
+        l = lx;
+        k = (out[r][l].u == x) ? out[r][l].v : out[r][l].u;
+      }
+    }
+    // layer r+1: lane l continues with its kept channel as the first operand
+    for (int l = 0; l < 64; ++l) {
+      out[r][l].keep_v = keep[l] == out[r][l].v;
+      out[r + 1][l] = LaneRec{keep[l], nxt[keep[l]], 0, 0, false};
+    }
+    // hand-off slots: writer lane l (8-lane block l/8) -> reader lane l2 (16-lane block l2/16);
+    // slot = 16 (l2/16) + rho with rho distinct in each reader block (reads: rows distinct mod 16)
+    // and rho mod 8 distinct in each writer block (writes: rows distinct mod 8)
+    int reader[64], wl[64], hr[64], col[64];
+    for (int l2 = 0; l2 < 64; ++l2) reader[lane_at[out[r + 1][l2].v]] = l2;   // v of l2 is handed off by its layer-r lane
+    int seen_rb[4] = {0, 0, 0, 0};
+    for (int l = 0; l < 64; ++l) {
+      const int rb = reader[l] / 16;
+      wl[l] = l / 8;
+      hr[l] = 2 * rb + (seen_rb[rb]++ < 8 ? 0 : 1);   // halves of the reader block, 8 edges each
+    }
+    if (!colour_regular(8, 8, wl, hr, col)) return false;
+    for (int l = 0; l < 64; ++l) {
+      const int slot = 16 * (reader[l] / 16) + col[l] + 8 * (hr[l] & 1);
+      out[r][l].wslot = slot;
+      out[r + 1][reader[l]].rslot = slot;
+    }
+  }
+  return true;
+}
+
 }  // namespace pq
 
 extern "C" {
@@ -223,30 +332,45 @@ int pq_build_records(const int16_t* pairs_h, const uint16_t* theta_h, int K, voi
       }
     }
   std::vector<uint8_t> out(static_cast<size_t>(PQ_LAYERS) * half * 8);
-  for (int r = 0; r < PQ_LAYERS; ++r)
-    for (int g = 0; g < G; ++g) {
-      int pi[64], pj[64], tail[64], head[64], lane_of[64];
-      uint16_t c16[64], s16[64];
+  for (int g = 0; g < G; ++g) {
+    int pi[PQ_LAYERS][64], pj[PQ_LAYERS][64];
+    uint16_t c16[PQ_LAYERS][64], s16[PQ_LAYERS][64];
+    int pair_of[PQ_LAYERS][128];
+    for (int r = 0; r < PQ_LAYERS; ++r)
       for (int q = 0; q < 64; ++q) {
         const size_t pidx = static_cast<size_t>(r) * K + g * PQ_GROUP + 2 * q;
-        pi[q] = pairs_h[pidx];
-        pj[q] = pairs_h[pidx + 1];
+        pi[r][q] = pairs_h[pidx];
+        pj[r][q] = pairs_h[pidx + 1];
+        pair_of[r][pi[r][q]] = q;
+        pair_of[r][pj[r][q]] = q;
         const double th = f16_to_double(theta_h[static_cast<size_t>(r) * half + g * 64 + q]);
-        c16[q] = f16_from_double(std::cos(th));
-        s16[q] = f16_from_double(std::sin(th));
+        c16[r][q] = f16_from_double(std::cos(th));
+        s16[r][q] = f16_from_double(std::sin(th));
       }
-      if (!order_layer(pi, pj, tail, head, lane_of))
-        return set_error(PQ_ERR_RECORDS, "pairs layer %d group %d: lane ordering failed", r, g);
-      for (int q = 0; q < 64; ++q) {
-        // listing the pair as (j, i) is the same rotation with sin negated
-        const uint16_t s = (tail[q] == pi[q]) ? s16[q] : static_cast<uint16_t>(s16[q] ^ 0x8000);
-        const uint32_t ij = static_cast<uint32_t>(tail[q]) | (static_cast<uint32_t>(head[q]) << 8);
-        uint8_t* dst = out.data() + (static_cast<size_t>(r) * half + g * 64 + lane_of[q]) * 8;
-        std::memcpy(dst, &ij, 4);
-        std::memcpy(dst + 4, &c16[q], 2);
-        std::memcpy(dst + 6, &s, 2);
+    LaneRec lr[PQ_LAYERS][64];
+    if (!chain_group(pi, pj, lr))
+      return set_error(PQ_ERR_RECORDS, "pairs group %d: lane ordering failed", g);
+    for (int r = 0; r < PQ_LAYERS; ++r)
+      for (int l = 0; l < 64; ++l) {
+        const LaneRec& e = lr[r][l];
+        const int q = pair_of[r][e.u];
+        // (c, s) of the pair listed as (u, v): listing it as (j, i) negates sin
+        const uint16_t c = c16[r][q];
+        const uint16_t sn = (pi[r][q] == e.u) ? s16[r][q] : static_cast<uint16_t>(s16[r][q] ^ 0x8000);
+        // kept output u: keep = c u + s v, other = c v - s u  -> (f1, f2) = (c, s)
+        // kept output v: keep = -s u + c v, other = s v + c u -> (f1, f2) = (-s, c)
+        const bool kv = (r + 1 < PQ_LAYERS) && e.keep_v;
+        const uint16_t f1 = kv ? static_cast<uint16_t>(sn ^ 0x8000) : c;
+        const uint16_t f2 = kv ? c : sn;
+        const uint32_t w = static_cast<uint32_t>(e.u) | (static_cast<uint32_t>(e.v) << 8) |
+                           (kv ? 0x8000u : 0u) | (static_cast<uint32_t>(r > 0 ? e.rslot : 0) << 16) |
+                           (static_cast<uint32_t>(r + 1 < PQ_LAYERS ? e.wslot : 0) << 24);
+        uint8_t* dst = out.data() + (static_cast<size_t>(r) * half + g * 64 + l) * 8;
+        std::memcpy(dst, &w, 4);
+        std::memcpy(dst + 4, &f1, 2);
+        std::memcpy(dst + 6, &f2, 2);
       }
-    }
+  }
   std::memcpy(rec_h, out.data(), out.size());
   return PQ_OK;
 }

@@ -14,9 +14,13 @@
 // rotation records in registers and carries 8 tokens per step as two quads of 4: lane
 // (t = lane/16, c = lane%16) loads 16 bytes (channels 8c..8c+7) of token t of each quad, the
 // next step's loads in flight while the current step computes. The scaled values go to LDS
-// token-minor, channel ch of a quad in the 16-byte row ch + ch/8 (4 tokens), so the layer
-// updates are one 16-byte read and write per pair end and 4 tokens per lane; the record lane
-// order (pq_build_records) keeps those accesses and the transposing scalar ones free of bank
+// token-minor, channel ch of a quad in the 16-byte row ch + ch/8 (4 tokens, the quad image).
+// The layers then move 16 bytes (4 tokens) per LDS access: the first layer reads both channels
+// of each lane's pair from the image, each later one keeps one channel of the previous layer's
+// output in registers and takes the other from a hand-off row (one read and one write per lane
+// and layer instead of two of each; on gfx950 a 16-byte LDS write costs about 2.5x a read), and
+// the last layer writes both back to the image (rot_layers). The record lane order and hand-off
+// rows (pq_build_records) keep those accesses and the transposing scalar ones free of bank
 // conflicts. amax and the row-sum are reductions over the 16 lanes of a token (DPP).
 //
 // Encoding: fl32(v * inv) + 0 (which turns -0 into +0) goes straight to the hardware convert.
@@ -37,6 +41,117 @@ constexpr int kProQuadBytes = 144 * 16;      // 128 channel rows + 15 pad rows, 
 constexpr int kProUnits = 16384;             // aim for about this many wave units
 
 __device__ __forceinline__ uint32_t lds_row_bytes(uint32_t ch) { return (ch + (ch >> 3)) << 4; }
+
+// The 8 rotation layers of one token-group, driven by the lane's records (layout in pq.h): on
+// entry every channel ch of a quad sits in the 16-byte image row lds_row(ch) (4 tokens), on exit
+// the rotated channels are back in those rows. Layer 0 reads both of the lane's channels from the
+// image; afterwards a lane keeps one output of each layer in registers (the next layer's first
+// operand) and passes the other through a hand-off row of LDS to the lane that needs it, so
+// layers 1..6 read and write one row per quad instead of two; layer 7 writes both outputs to the
+// image. Per token: keep = f1*u + f2*v, other = g*v + d*u, every product and sum rounding to
+// binary32 (this TU has contraction off) -- the pair's rotation, with the two outputs in either
+// order.
+struct RotRec {
+  uint32_t u0, v0;                 // layer 0: image rows of u and v (bytes)
+  uint32_t rd[PQ_LAYERS];          // layers 1..7: hand-off row read (bytes)
+  uint32_t wr[PQ_LAYERS];          // layers 0..6: hand-off row written (bytes)
+  uint32_t u7, v7;                 // layer 7: image rows of u and v (bytes)
+  float f1[PQ_LAYERS], f2[PQ_LAYERS], g[PQ_LAYERS], d[PQ_LAYERS];
+};
+
+__device__ __forceinline__ void rot_decode(const uint2 (&q)[PQ_LAYERS], RotRec& R) {
+  R.u0 = lds_row_bytes(q[0].x & 0x7Fu);
+  R.v0 = lds_row_bytes((q[0].x >> 8) & 0x7Fu);
+  R.u7 = lds_row_bytes(q[PQ_LAYERS - 1].x & 0x7Fu);
+  R.v7 = lds_row_bytes((q[PQ_LAYERS - 1].x >> 8) & 0x7Fu);
+#pragma unroll
+  for (int r = 0; r < PQ_LAYERS; ++r) {
+    R.rd[r] = ((q[r].x >> 16) & 0xFFu) << 4;
+    R.wr[r] = (q[r].x >> 24) << 4;
+    const uint32_t keep_v = (q[r].x >> 15) & 1u;   // v's output kept: (g, d) = (-f1, f2), else (f1, -f2)
+    R.f1[r] = f16_to_f32(q[r].y);
+    R.f2[r] = f16_to_f32(q[r].y >> 16);
+    R.g[r] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, R.f1[r]) ^ (keep_v << 31));
+    R.d[r] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, R.f2[r]) ^ ((keep_v ^ 1u) << 31));
+  }
+}
+
+// NQ quad images at buf + q * QB.
+template <int NQ, int QB>
+__device__ __forceinline__ void rot_layers(uint8_t* buf, const RotRec& R) {
+  float4 reg[NQ];
+#pragma unroll
+  for (int r = 0; r < PQ_LAYERS; ++r) {
+    float4 a[NQ], b[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      a[q] = r == 0 ? *reinterpret_cast<const float4*>(buf + q * QB + R.u0) : reg[q];
+      b[q] = *reinterpret_cast<const float4*>(buf + q * QB + (r == 0 ? R.v0 : R.rd[r]));
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const float av[4] = {a[q].x, a[q].y, a[q].z, a[q].w}, bv[4] = {b[q].x, b[q].y, b[q].z, b[q].w};
+      float kp[4], ot[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x1 = R.f1[r] * av[k], x2 = R.f2[r] * bv[k];
+        const float y1 = R.g[r] * bv[k], y2 = R.d[r] * av[k];
+        kp[k] = x1 + x2;
+        ot[k] = y1 + y2;
+      }
+      if (r + 1 < PQ_LAYERS) {
+        reg[q] = make_float4(kp[0], kp[1], kp[2], kp[3]);
+        *reinterpret_cast<float4*>(buf + q * QB + R.wr[r]) = make_float4(ot[0], ot[1], ot[2], ot[3]);
+      } else {
+        *reinterpret_cast<float4*>(buf + q * QB + R.u7) = make_float4(kp[0], kp[1], kp[2], kp[3]);
+        *reinterpret_cast<float4*>(buf + q * QB + R.v7) = make_float4(ot[0], ot[1], ot[2], ot[3]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// The same layers on one quad image, each record decoded where its layer runs (for kernels that
+// load a group's records just before rotating it).
+template <int NQ, int QB>
+__device__ __forceinline__ void rot_layers_q(uint8_t* buf, const uint2 (&q)[PQ_LAYERS]) {
+  float4 reg[NQ];
+#pragma unroll
+  for (int r = 0; r < PQ_LAYERS; ++r) {
+    const uint32_t x = q[r].x;
+    const uint32_t keep_v = (x >> 15) & 1u;
+    const float f1 = f16_to_f32(q[r].y), f2 = f16_to_f32(q[r].y >> 16);
+    const float gg = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f1) ^ (keep_v << 31));
+    const float dd = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f2) ^ ((keep_v ^ 1u) << 31));
+    const uint32_t ra = lds_row_bytes(x & 0x7Fu), rb = lds_row_bytes((x >> 8) & 0x7Fu);
+    float4 a[NQ], b[NQ];
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      a[qd] = r == 0 ? *reinterpret_cast<const float4*>(buf + qd * QB + ra) : reg[qd];
+      b[qd] = *reinterpret_cast<const float4*>(buf + qd * QB + (r == 0 ? rb : ((x >> 16) & 0xFFu) << 4));
+    }
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      const float av[4] = {a[qd].x, a[qd].y, a[qd].z, a[qd].w}, bv[4] = {b[qd].x, b[qd].y, b[qd].z, b[qd].w};
+      float kp[4], ot[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x1 = f1 * av[k], x2 = f2 * bv[k];
+        const float y1 = gg * bv[k], y2 = dd * av[k];
+        kp[k] = x1 + x2;
+        ot[k] = y1 + y2;
+      }
+      if (r + 1 < PQ_LAYERS) {
+        reg[qd] = make_float4(kp[0], kp[1], kp[2], kp[3]);
+        *reinterpret_cast<float4*>(buf + qd * QB + ((x >> 24) << 4)) = make_float4(ot[0], ot[1], ot[2], ot[3]);
+      } else {
+        *reinterpret_cast<float4*>(buf + qd * QB + ra) = make_float4(kp[0], kp[1], kp[2], kp[3]);
+        *reinterpret_cast<float4*>(buf + qd * QB + rb) = make_float4(ot[0], ot[1], ot[2], ot[3]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
 
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {
@@ -122,15 +237,12 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(
   const int t = lane >> 4, c = lane & 15;
   const int half = K >> 1;
 
-  uint32_t ta[PQ_LAYERS], ha[PQ_LAYERS];
-  float cr[PQ_LAYERS], sr[PQ_LAYERS];
+  RotRec R;
+  {
+    uint2 q[PQ_LAYERS];
 #pragma unroll
-  for (int r = 0; r < PQ_LAYERS; ++r) {
-    const uint2 q = rec[(static_cast<size_t>(p) * PQ_LAYERS + r) * half + g * 64 + lane];
-    ta[r] = lds_row_bytes(q.x & 0x7Fu);   // channel indices are 0..127
-    ha[r] = lds_row_bytes((q.x >> 8) & 0x7Fu);
-    cr[r] = f16_to_f32(q.y);
-    sr[r] = f16_to_f32(q.y >> 16);
+    for (int r = 0; r < PQ_LAYERS; ++r) q[r] = rec[(static_cast<size_t>(p) * PQ_LAYERS + r) * half + g * 64 + lane];
+    rot_decode(q, R);
   }
   const uint32_t* csp = reinterpret_cast<const uint32_t*>(cs + static_cast<size_t>(p) * K + g * 128 + 8 * c);
   const uint32_t cw[4] = {csp[0], csp[1], csp[2], csp[3]};
@@ -161,31 +273,7 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(
       }
     }
     __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int r = 0; r < PQ_LAYERS; ++r) {
-      float4 a[kProQuads], b[kProQuads];
-#pragma unroll
-      for (int q = 0; q < kProQuads; ++q) {
-        a[q] = *reinterpret_cast<const float4*>(buf + q * kProQuadBytes + ta[r]);
-        b[q] = *reinterpret_cast<const float4*>(buf + q * kProQuadBytes + ha[r]);
-      }
-#pragma unroll
-      for (int q = 0; q < kProQuads; ++q) {
-        const float av[4] = {a[q].x, a[q].y, a[q].z, a[q].w};
-        const float bv[4] = {b[q].x, b[q].y, b[q].z, b[q].w};
-        float na[4], nb[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float ca = cr[r] * av[k], sb = sr[r] * bv[k];
-          const float cb = cr[r] * bv[k], sa = sr[r] * av[k];
-          na[k] = ca + sb;
-          nb[k] = cb - sa;
-        }
-        *reinterpret_cast<float4*>(buf + q * kProQuadBytes + ta[r]) = make_float4(na[0], na[1], na[2], na[3]);
-        *reinterpret_cast<float4*>(buf + q * kProQuadBytes + ha[r]) = make_float4(nb[0], nb[1], nb[2], nb[3]);
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
+    rot_layers<kProQuads, kProQuadBytes>(buf, R);
     float v[kProQuads][8], inv[kProQuads], asg[kProQuads];
     uint32_t w[kProQuads][2];
     uint32_t bad = 0;
@@ -327,25 +415,7 @@ __global__ __launch_bounds__(64 * kTokWaves) void rotate_quant_tok_kernel(
         *reinterpret_cast<float*>(slot + (2 * i + 1) * 16) = half_hi(xw[i]) * half_hi(cs4[i]);
       }
       __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int r = 0; r < PQ_LAYERS; ++r) {
-        const uint32_t ta = lds_row_bytes(q[r].x & 0x7Fu), ha = lds_row_bytes((q[r].x >> 8) & 0x7Fu);
-        const float cr = f16_to_f32(q[r].y), sr = f16_to_f32(q[r].y >> 16);
-        const float4 a = *reinterpret_cast<const float4*>(buf + ta);
-        const float4 b = *reinterpret_cast<const float4*>(buf + ha);
-        const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-        float na[4], nb[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float ca = cr * av[k], sb = sr * bv[k];
-          const float cb = cr * bv[k], sa = sr * av[k];
-          na[k] = ca + sb;
-          nb[k] = cb - sa;
-        }
-        *reinterpret_cast<float4*>(buf + ta) = make_float4(na[0], na[1], na[2], na[3]);
-        *reinterpret_cast<float4*>(buf + ha) = make_float4(nb[0], nb[1], nb[2], nb[3]);
-        __builtin_amdgcn_wave_barrier();
-      }
+      rot_layers_q<1, kProQuadBytes>(buf, q);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         park[j][i] = *reinterpret_cast<const float*>(slot + i * 16);
@@ -508,25 +578,7 @@ __global__ __launch_bounds__(64 * kTokWaves) void add_rms_rotate_quant_kernel(
         *reinterpret_cast<float*>(slot + (2 * i + 1) * 16) = half_hi(hp[j][i]) * half_hi(cs4[i]);
       }
       __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int r = 0; r < PQ_LAYERS; ++r) {
-        const uint32_t ta = lds_row_bytes(q[r].x & 0x7Fu), ha = lds_row_bytes((q[r].x >> 8) & 0x7Fu);
-        const float cr = f16_to_f32(q[r].y), sr = f16_to_f32(q[r].y >> 16);
-        const float4 a = *reinterpret_cast<const float4*>(buf + ta);
-        const float4 b = *reinterpret_cast<const float4*>(buf + ha);
-        const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-        float na[4], nb[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float ca = cr * av[k], sb = sr * bv[k];
-          const float cb = cr * bv[k], sa = sr * av[k];
-          na[k] = ca + sb;
-          nb[k] = cb - sa;
-        }
-        *reinterpret_cast<float4*>(buf + ta) = make_float4(na[0], na[1], na[2], na[3]);
-        *reinterpret_cast<float4*>(buf + ha) = make_float4(nb[0], nb[1], nb[2], nb[3]);
-        __builtin_amdgcn_wave_barrier();
-      }
+      rot_layers_q<1, kProQuadBytes>(buf, q);
       float v[8];
       float gmax = 0.0f;
 #pragma unroll

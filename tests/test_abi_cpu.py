@@ -10,7 +10,10 @@ import pytest
 
 import rotated_w4a8_group_amd as pq
 import synth
+from oracle import prologue as oprologue
 from oracle import records as orec
+
+import lanes
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pq.h")
@@ -36,15 +39,15 @@ def test_abi_version():
     assert pq.lib().pq_abi_version() == int(m.group(1))
 
 
-def _canon(i, j, c16, s16):
-    """A pair listed as (j, i) with sin negated is the same rotation."""
-    if i < j:
-        return (int(i), int(j), int(c16), int(s16))
-    return (int(j), int(i), int(c16), int(s16) ^ 0x8000)
+def _ref_rotations(ref, r, sl):
+    return sorted((int(i), int(j), int(c), int(s)) if i < j else (int(j), int(i), int(c), int(s) ^ 0x8000)
+                  for i, j, c, s in zip(ref["i"][r, sl], ref["j"][r, sl], ref["cos16"][r, sl], ref["sin16"][r, sl]))
 
 
 @pytest.mark.parametrize("wl_name", ["tiny", "qkv"])
 def test_records_match_oracle_up_to_lane_order(wl_name):
+    """Each (layer, group) of records applies exactly the oracle's 64 rotations, in some lane
+    order and orientation."""
     wl = synth.WORKLOADS[wl_name]
     pl, tl, _ = synth.rotations(wl)
     for pairs, theta in zip(pl, tl):
@@ -52,46 +55,17 @@ def test_records_match_oracle_up_to_lane_order(wl_name):
             pairs, theta = pairs[:, :1024], theta[:, :512]
         lib = pq.build_records(pairs, theta)          # [8, K/2, 8]
         ref = orec.build(pairs, theta)
-        ij = lib[..., :4].copy().view(np.uint32)[..., 0]
-        li, lj = ij & 0xFF, (ij >> 8) & 0xFF
-        lc = lib[..., 4:6].copy().view(np.uint16)[..., 0]
-        ls = lib[..., 6:8].copy().view(np.uint16)[..., 0]
-        K = pairs.shape[1]
+        d = lanes.decode(lib)
         for r in range(8):
-            for g in range(K // 128):
+            for g in range(pairs.shape[1] // 128):
                 sl = slice(64 * g, 64 * g + 64)
-                a = sorted(_canon(*t) for t in zip(li[r, sl], lj[r, sl], lc[r, sl], ls[r, sl]))
-                b = sorted(_canon(*t) for t in zip(ref["i"][r, sl], ref["j"][r, sl],
-                                                   ref["cos16"][r, sl], ref["sin16"][r, sl]))
-                assert a == b, (r, g)
-
-
-def _lds_row(ch):
-    return ch + (ch >> 3)
-
-
-def _check_lane_order(lib):
-    """In the prologue a quad of tokens keeps channel ch in the 16-byte LDS row ch + ch//8 and
-    lane l reads and writes the rows of its record's two channels. 16-byte accesses are served
-    16 lanes (64 banks) or 8 lanes (32 banks) at a time, so the rows must be distinct mod 16
-    in every 16-lane block and mod 8 in every 8-lane half-block, for the first channels and for
-    the second channels separately."""
-    ij = lib[..., :4].copy().view(np.uint32)[..., 0]
-    for r in range(ij.shape[0]):
-        for g in range(ij.shape[1] // 64):
-            w = ij[r, 64 * g:64 * g + 64].astype(int)
-            for col in (w & 0xFF, (w >> 8) & 0xFF):
-                row = _lds_row(col)
-                for blk in range(4):
-                    assert len(set(row[16 * blk:16 * blk + 16] % 16)) == 16, (r, g, blk)
-                for hb in range(8):
-                    assert len(set(row[8 * hb:8 * hb + 8] % 8)) == 8, (r, g, hb)
+                assert lanes.canonical(d, r, sl) == _ref_rotations(ref, r, sl), (r, g)
 
 
 def test_records_lane_order_is_bank_conflict_free():
     wl = synth.WORKLOADS["qkv"]
     pl, tl, _ = synth.rotations(wl)
-    _check_lane_order(pq.build_records(pl[1][:, :2048], tl[1][:, :1024]))
+    lanes.check_lanes(pq.build_records(pl[1][:, :2048], tl[1][:, :1024]))
 
 
 @pytest.mark.parametrize("seed", range(4))
@@ -110,7 +84,7 @@ def test_records_lane_order_any_pairing(seed):
                 perm = np.arange(128)                      # (0,1), (2,3), ...: same 8-block
             elif kind == 2:
                 # pair ch with the channel whose row is 16 higher: equal rows mod 16
-                order = sorted(range(128), key=lambda ch: (_lds_row(ch) % 16, ch))
+                order = sorted(range(128), key=lambda ch: (lanes.lds_row(ch) % 16, ch))
                 perm = np.array(order)
             else:
                 perm = np.concatenate([np.arange(0, 128, 2), np.arange(1, 128, 2)])
@@ -119,19 +93,19 @@ def test_records_lane_order_any_pairing(seed):
             pairs[r, 128 * g:128 * g + 128] = perm
     theta = rng.standard_normal((8, K // 2)).astype(np.float16)
     lib = pq.build_records(pairs, theta)
-    _check_lane_order(lib)
-    # and the records still hold exactly the given rotations
-    ij = lib[..., :4].copy().view(np.uint32)[..., 0]
+    lanes.check_lanes(lib)
+    # and the records still hold exactly the given rotations, and compute them
     ref = orec.build(pairs, theta)
-    lc = lib[..., 4:6].copy().view(np.uint16)[..., 0]
-    ls = lib[..., 6:8].copy().view(np.uint16)[..., 0]
+    d = lanes.decode(lib)
     for r in range(8):
         for g in range(K // 128):
             sl = slice(64 * g, 64 * g + 64)
-            a = sorted(_canon(*t) for t in zip(ij[r, sl] & 0xFF, (ij[r, sl] >> 8) & 0xFF, lc[r, sl], ls[r, sl]))
-            b = sorted(_canon(*t) for t in zip(ref["i"][r, sl], ref["j"][r, sl],
-                                               ref["cos16"][r, sl], ref["sin16"][r, sl]))
-            assert a == b, (r, g)
+            assert lanes.canonical(d, r, sl) == _ref_rotations(ref, r, sl), (r, g)
+    cs = np.ones(K, np.float16)
+    x = rng.standard_normal((5, K)).astype(np.float16)
+    want = oprologue.rotate_f32(x, ref, cs)
+    got = lanes.simulate(lib, x.astype(np.float32))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
 def test_records_reject_bad_pairs():
@@ -381,3 +355,38 @@ def test_plan_partitions_merges_only_adjacent_and_exact():
     with pytest.raises(pq.PQError) as e:       # columns not a multiple of 16
         pq.plan_partitions([[100] + a[1:]])
     assert e.value.code == -2
+
+
+@pytest.mark.parametrize("wl_name", ["tiny", "qkv", "decode_m1"])
+def test_records_chain_computes_the_oracle_rotation(wl_name):
+    """Driving the prologue's register / LDS dataflow with the records alone (first layer from
+    the image, later layers from a register and a hand-off row, last layer back to the image)
+    gives the oracle's float32 rotation bit for bit, on every partition of the workload."""
+    wl = synth.WORKLOADS[wl_name]
+    pl, tl, cl = synth.rotations(wl)
+    x = synth.activations(wl, M=6)
+    K = min(wl.K, 2048)
+    for pairs, theta, cs in zip(pl, tl, cl):
+        pairs, theta, cs = pairs[:, :K], theta[:, :K // 2], cs[:K]
+        lib = pq.build_records(pairs, theta)
+        lanes.check_lanes(lib)
+        xv = x[:, :K].astype(np.float32) * cs.astype(np.float32)
+        want = oprologue.rotate_f32(x[:, :K], orec.build(pairs, theta), cs)
+        got = lanes.simulate(lib, xv)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_records_chain_simulation_catches_a_wrong_slot():
+    """The simulation is sensitive to the routing: one hand-off row swapped between two lanes of
+    a layer changes the result."""
+    wl = synth.WORKLOADS["tiny"]
+    pl, tl, cl = synth.rotations(wl)
+    lib = pq.build_records(pl[0], tl[0]).copy()
+    x = synth.activations(wl).astype(np.float32)
+    good = lanes.simulate(lib, x)
+    w = lib[3, :, :4].copy().view(np.uint32)[:, 0]
+    r0, r1 = (w[5] >> 16) & 0xFF, (w[9] >> 16) & 0xFF
+    w[5] = (w[5] & ~np.uint32(0xFF0000)) | (r1 << 16)
+    w[9] = (w[9] & ~np.uint32(0xFF0000)) | (r0 << 16)
+    lib[3, :, :4] = w.view(np.uint8).reshape(-1, 4)
+    assert not np.array_equal(lanes.simulate(lib, x).view(np.uint32), good.view(np.uint32))
