@@ -262,20 +262,34 @@ __global__ void zpe_act_kernel(const float* __restrict__ ASG, const float* __res
   const int mt = static_cast<int>(rest % MT);
   const int p = static_cast<int>(rest / MT);
   const int row = 16 * mt + (l & 15);
-  uint32_t h[8];
+  // every load first (clamped to valid memory), then the arithmetic, then the stores: a store
+  // between loads would make each load wait for the previous store
+  const size_t rbase = (static_cast<size_t>(p) * M + min(row, M - 1)) * G;
+  float av[8], rv[8];
+  int piece[8], gg[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int kp = 32 * c + 8 * (l >> 4) + e;
+    piece[e] = (kp < 3 * G && row < M) ? kp / G : -1;
+    gg[e] = kp < 3 * G ? kp % G : 0;
+    av[e] = kTok ? 1.0f : ASG[rbase + gg[e]];
+    rv[e] = RS[rbase + gg[e]];
+  }
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
     uint32_t v = 0;
-    if (kp < 3 * G && row < M) {
-      const int piece = kp / G, g = kp % G;
-      const size_t o = (static_cast<size_t>(p) * M + row) * G + g;
-      const float ar = kTok ? RS[o] : ASG[o] * RS[o];
-      if (!kTok && piece == 0) asgt[(static_cast<size_t>(p) * G + g) * M + row] = ASG[o];   // [P][G][M] copy
+    if (piece[e] >= 0) {
+      const float ar = kTok ? rv[e] : av[e] * rv[e];
       const uint32_t a1 = f32_to_bf16(ar);
-      v = ((piece == 2) ? f32_to_bf16(ar - bf16_to_f32(a1)) : a1) ^ 0x8000u;   // negated
+      v = ((piece[e] == 2) ? f32_to_bf16(ar - bf16_to_f32(a1)) : a1) ^ 0x8000u;   // negated
     }
     h[e] = v;
+  }
+  if (!kTok) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (piece[e] == 0) asgt[(static_cast<size_t>(p) * G + gg[e]) * M + row] = av[e];   // [P][G][M] copy
   }
   zpa[idx] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
