@@ -376,17 +376,21 @@ def test_records_chain_computes_the_oracle_rotation(wl_name):
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
-def test_records_chain_simulation_catches_a_wrong_slot():
+@pytest.mark.parametrize("layer,shift", [(3, 16), (3, 24), (0, 24), (7, 16)])
+def test_records_chain_simulation_catches_a_wrong_slot(layer, shift):
     """The simulation is sensitive to the routing: one hand-off row swapped between two lanes of
-    a layer changes the result."""
+    a layer changes the result (a middle layer's read and write rows, layer 0's write row and
+    layer 7's read row)."""
     wl = synth.WORKLOADS["tiny"]
     pl, tl, cl = synth.rotations(wl)
     lib = pq.build_records(pl[0], tl[0]).copy()
     x = synth.activations(wl).astype(np.float32)
     good = lanes.simulate(lib, x)
-    w = lib[3, :, :4].copy().view(np.uint32)[:, 0]
-    r0, r1 = (w[5] >> 16) & 0xFF, (w[9] >> 16) & 0xFF
-    w[5] = (w[5] & ~np.uint32(0xFF0000)) | (r1 << 16)
-    w[9] = (w[9] & ~np.uint32(0xFF0000)) | (r0 << 16)
-    lib[3, :, :4] = w.view(np.uint8).reshape(-1, 4)
+    w = lib[layer, :, :4].copy().view(np.uint32)[:, 0]
+    mask = np.uint32(0xFF << shift)
+    r0, r1 = w[5] & mask, w[9] & mask
+    assert r0 != r1
+    w[5] = (w[5] & ~mask) | r1
+    w[9] = (w[9] & ~mask) | r0
+    lib[layer, :, :4] = w.view(np.uint8).reshape(-1, 4)
     assert not np.array_equal(lanes.simulate(lib, x).view(np.uint32), good.view(np.uint32))
