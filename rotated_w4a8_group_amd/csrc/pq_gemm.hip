@@ -822,10 +822,14 @@ __device__ __forceinline__ void prefill_tile(
             acc[pm][nf][2] = __builtin_fmaf(s9[nf].z, T[2], acc[pm][nf][2]);
             acc[pm][nf][3] = __builtin_fmaf(s9[nf].w, T[3], acc[pm][nf][3]);
           } else {
-            acc[pm][nf][0] = __builtin_fmaf(as * s9[nf].x, T[0], acc[pm][nf][0]);
-            acc[pm][nf][1] = __builtin_fmaf(as * s9[nf].y, T[1], acc[pm][nf][1]);
-            acc[pm][nf][2] = __builtin_fmaf(as * s9[nf].z, T[2], acc[pm][nf][2]);
-            acc[pm][nf][3] = __builtin_fmaf(as * s9[nf].w, T[3], acc[pm][nf][3]);
+            // the four factors first, in registers of their own (the empty asm keeps the compiler
+            // from pairing each multiply with its dependent FMA through one temporary)
+            const float f0 = as * s9[nf].x, f1 = as * s9[nf].y, f2 = as * s9[nf].z, f3 = as * s9[nf].w;
+            asm volatile("" ::"v"(f0), "v"(f1), "v"(f2), "v"(f3));
+            acc[pm][nf][0] = __builtin_fmaf(f0, T[0], acc[pm][nf][0]);
+            acc[pm][nf][1] = __builtin_fmaf(f1, T[1], acc[pm][nf][1]);
+            acc[pm][nf][2] = __builtin_fmaf(f2, T[2], acc[pm][nf][2]);
+            acc[pm][nf][3] = __builtin_fmaf(f3, T[3], acc[pm][nf][3]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
