@@ -87,7 +87,8 @@ def test_producer_parity(name):
     _check(name, wl, x, r, w, pl, tl, cl, out, rows=rows)
 
 
-@pytest.mark.parametrize("M,K,splits", [(37, 640, (64, 32, 32)), (8, 17408, ()), (1, 128, ()), (5, 2176, (64, 64))])
+@pytest.mark.parametrize("M,K,splits", [(37, 640, (64, 32, 32)), (8, 17408, ()), (1, 128, ()), (5, 2176, (64, 64)),
+                                         (6, 18432, ()), (70, 18432, ())])
 def test_producer_shapes(M, K, splits):
     wl = synth.Workload("prod", 190 + M, M, K, 128, splits=splits)
     x, r, w = synth.activations(wl), synth.residual(wl), synth.norm_weight(wl)

@@ -94,6 +94,18 @@ def test_prologue_tok_edge_cases():
     _compare("one", A1, S1, R1, x1, pl1, tl1, cl1, np.arange(1))
 
 
+def test_prologue_tok_longest_row():
+    """K = 18432, the longest row the per-token kernel takes: 144 groups, exactly 9 parked in
+    every one of the 16 waves (no wave has a group slot left over), ragged token count, two
+    partitions; bit-exact on every row."""
+    wl = synth.Workload("tokmax", 83, 6, 18432, 128, splits=(64, 64))
+    print(f"[tok prologue longest row] M={wl.M} K={wl.K} P={wl.P}", flush=True)
+    x = synth.activations(wl)
+    pl, tl, cl = synth.rotations(wl)
+    A, S, R = _prologue_tok(wl, x, pl, tl, cl)
+    _compare("longest row", A, S, R, x, pl, tl, cl, np.arange(wl.M))
+
+
 def test_prologue_tok_rejects_long_rows():
     x = torch.zeros((4, 18560), dtype=torch.float16, device="cuda")
     rec = torch.zeros((1, 8, 18560 // 2, 8), dtype=torch.uint8, device="cuda")
