@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--ceilings-only", action="store_true",
                     help="only measure the HBM read and fp8 matrix-core ceilings and print them")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured ceilings")
+    ap.add_argument("--gemm-only", metavar="WORKLOAD",
+                    help="only run one synthetic workload (synth.WORKLOADS name): its prologue once, then "
+                         "5 GEMM calls (for counter passes that must see one shape)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -189,6 +192,10 @@ def main():
 
     if args.ceilings_only:
         print(json.dumps({"ceilings": measure_ceilings(torch, np)}), flush=True)
+        return
+
+    if args.gemm_only:
+        gemm_only(args.gemm_only, torch, np)
         return
     ceilings = None if args.no_ceilings else measure_ceilings(torch, np)
 
@@ -458,6 +465,31 @@ def producer_measurement(wl, pq, torch, np, dev, copies):
             "chain": "torch add + torch rms_norm (float32) + pq_rotate_quant",
             "timing": (f"HIP graph of {C} launches over {C} copies, per-launch median (p10, p90) of {REPS_SHORT} replays after ~30 ms of untimed replays" if short
                        else f"HIP events around each eager call, median (p10, p90) of {REPS_LONG} after ~30 ms of untimed calls, two alternating copies")}
+
+
+def gemm_only(name, torch, np, calls=5):
+    """One workload's prologue, then `calls` GEMM calls on its codes, nothing else (so that a
+    rocprofv3 counter pass sees the dispatches of one shape only)."""
+    import rotated_w4a8_group_amd as pq
+    import synth
+    wl = synth.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    M, K, N, G, P = wl.M, wl.K, wl.N, wl.G, wl.P
+    pl, tl, cl = synth.rotations(wl)
+    rec = torch.from_numpy(np.stack([pq.build_records(p, t) for p, t in zip(pl, tl)])).to(dev)
+    cs = torch.from_numpy(np.stack(cl)).to(dev)
+    x = torch.from_numpy(synth.activations(wl)).to(dev)
+    w = synth.weights(wl)
+    wpk, sz = pq.pack_weights(torch.from_numpy(w.qweight).to(dev), torch.from_numpy(w.qzeros).to(dev),
+                              torch.from_numpy(w.scales).to(dev))
+    A, S, R = pq.rotate_quant(x, rec, cs)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, pq.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
+    for _ in range(calls):
+        pq.gemm(A, S, R, wpk, sz, N, *wl.bounds, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"gemm_only": name, "M": M, "K": K, "N": N, "partitions": P, "calls": calls,
+                      "algorithmic_bytes": gemm_bytes(M, K, N, P)}), flush=True)
 
 
 def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False, w5=False):

@@ -577,7 +577,9 @@ void decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
 // k-steps of the same ring, their loads issued while the last groups compute; the bf16 tile is then
 // staged in LDS and written as whole rows.
 //
-// Tiles (PrefillMap): whole rounds of 256x256 tiles, one workgroup per CU; the tiles of the
+// Tiles (PrefillMap): whole rounds of 256x256 tiles, one workgroup per CU, numbered in bands of
+// 4 row tiles (tile_rc) so that the tiles an XCD runs at once share their activation and weight
+// codes in its L2; the tiles of the
 // last, partial round are cut into 2, 4 or 8 pieces (128x256, 128x128, 64x128) so that round
 // costs a fraction of a full one instead of a full round at low occupancy. Partition boundaries
 // that are not multiples of 256 switch the whole launch to 128x128 tiles (pieces 64x128).
@@ -638,10 +640,31 @@ __device__ __forceinline__ void store_tile_rows(const uint16_t* ot, uint16_t* __
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin; give each XCD a contiguous range of
-// tile numbers, and number tiles rows-fastest so that a range covers few column tiles.
+// tile numbers.
 __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
   const int q = ntiles / 8;
   return bid < 8 * q ? (bid % 8) * q + bid / 8 : bid;
+}
+
+// Tile number -> (row tile, column tile), in bands of kPfBand row tiles: within a band the
+// columns in order, within a column the band's rows (a last, shorter band takes the remaining
+// rows). An XCD's contiguous range of numbers then covers a few row tiles by many columns, so
+// the tiles it runs at once share both operands in its L2: 32 tiles as 4 rows x 8 columns need
+// 128 KiB of activation codes and 128 KiB of weight codes per group step (256x256 tiles),
+// where a column of 32 row tiles needs 1 MiB of activation codes.
+constexpr int kPfBand = 4;
+__device__ __forceinline__ void tile_rc(int t, int tiles_m, int tiles_n, int& row, int& col) {
+  const int bands = tiles_m / kPfBand, band_tiles = kPfBand * tiles_n;
+  const int band = t / band_tiles;
+  if (band < bands) {
+    const int rem = t - band * band_tiles;
+    col = rem / kPfBand;
+    row = band * kPfBand + rem % kPfBand;
+  } else {
+    const int last = tiles_m - bands * kPfBand, rem = t - bands * band_tiles;
+    col = rem / last;
+    row = bands * kPfBand + rem % last;
+  }
 }
 
 template <int TM, int TN, int WM, int WN, bool kTok, bool kI8, bool kW5, int S = kPfStages>
@@ -882,6 +905,7 @@ __device__ __forceinline__ void prefill_tile(
 enum PfShape : int { kPfWide = 0, kPfNarrow = 1 };
 struct PrefillMap {
   int tiles_m;   // whole tiles per tile column
+  int tiles_n;   // whole tiles per tile row
   int ntiles;    // whole tiles
   int full;      // workgroups that run whole tiles (whole rounds); the rest run pieces
   int split;     // pieces per remaining tile: 1, 2, 4 or 8 (wide) / 1 or 2 (narrow)
@@ -901,7 +925,9 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(
   const int big = piece ? map.full + (b - map.full) / map.split : b;
   const int r = piece ? (b - map.full) % map.split : 0;
   const int t = xcd_tile(big, map.ntiles);
-  int m0 = (t % map.tiles_m) * bm, n0 = (t / map.tiles_m) * bn;
+  int trow, tcol;
+  tile_rc(t, map.tiles_m, map.tiles_n, trow, tcol);
+  int m0 = trow * bm, n0 = tcol * bn;
   const int split = piece ? map.split : 1;
   // piece r of a whole tile: split 2 -> 2 row halves; 4 -> 2 x 2 quarters; 8 -> 4 row x 2 column
   if (split == 2) m0 += (bm / 2) * r;
@@ -937,7 +963,8 @@ PrefillMap prefill_map(int M, int N, int shape, int cus) {
   const int bm = shape == kPfWide ? 256 : 128, bn = shape == kPfNarrow ? 128 : 256;
   m.shape = shape;
   m.tiles_m = (M + bm - 1) / bm;
-  const int64_t nt = static_cast<int64_t>(m.tiles_m) * ((N + bn - 1) / bn);
+  m.tiles_n = (N + bn - 1) / bn;
+  const int64_t nt = static_cast<int64_t>(m.tiles_m) * m.tiles_n;
   m.ntiles = static_cast<int>(nt);
   const int64_t full = (nt / cus) * cus, rem = nt - full;
   m.full = static_cast<int>(full);
