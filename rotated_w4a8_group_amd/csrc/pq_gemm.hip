@@ -570,8 +570,8 @@ void decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
 // arrives as whole 128-byte rows (8 rows per load, fully used cache lines) with the 16-byte chunk
 // index XOR-swizzled by (row%8) ^ ((row/8)%2): each 16-lane quarter of a fragment read then
 // covers the 64 LDS banks once (measured on gfx950: (row/2)%8 and row%8 read ~40% slower); the
-// weight image is already in fragment order (each lane reads 16 contiguous bytes). Per group and wave the
-// products T = MFMA(codes_g, A_g) are folded as acc += (asg * 512 sc) * T (2 VALU per output),
+// weight image is already in fragment order (each lane reads 16 contiguous bytes). Per group and
+// wave the products T = MFMA(codes_g, A_g) are folded as acc += (asg * 512 sc) * T (2 VALU per output),
 // each row fragment's products issued before the previous fragment's fold. The zero-point term is
 // subtracted as a bf16 matrix-core product (pack_zpe_kernel / zpe_act_kernel operands) in KC more
 // k-steps of the same ring, their loads issued while the last groups compute; the bf16 tile is then
@@ -579,10 +579,10 @@ void decode_map(int N, int pb1, int pb2, int cus, DecodeMap* map) {
 //
 // Tiles (PrefillMap): whole rounds of 256x256 tiles, one workgroup per CU, numbered in bands of
 // 4 row tiles (tile_rc) so that the tiles an XCD runs at once share their activation and weight
-// codes in its L2; the tiles of the
-// last, partial round are cut into 2, 4 or 8 pieces (128x256, 128x128, 64x128) so that round
-// costs a fraction of a full one instead of a full round at low occupancy. Partition boundaries
-// that are not multiples of 256 switch the whole launch to 128x128 tiles (pieces 64x128).
+// codes in its L2; the tiles of the last, partial round are cut into 2, 4 or 8 pieces (128x256,
+// 128x128, 64x128) so that round costs a fraction of a full one instead of a full round at low
+// occupancy. Partition boundaries that are not multiples of 256 switch the whole launch to
+// 128x128 tiles (pieces 64x128).
 constexpr int kPfStages = 3;
 constexpr int kPfWaves = 8;
 constexpr int kPfLds = kPfStages * 51200;   // the 256x256 ring (the largest)
