@@ -255,7 +255,8 @@ int pq_gemm_i8(const int8_t* a_d, const float* asg_d, const float* rs_d, int M, 
  * pq_gemm5: arguments as pq_gemm with wpk5_d/sz_d from pq_pack_weights5 (N % 32 == 0):
  *   y[m, n] = bf16_rne( sum_g asg_p[m,g] * ( sc[g,n] * sum_{k in g} D(A_p[m,k]) * (c[k,n] - 16)
  *                                            - fl16(sc[g,n]*(zp[g,n]-16)) * rs_p[m,g] ) )
- *   Same workspace as pq_gemm (pq_gemm_workspace_bytes); M > 16 runs 128x128 tiles.
+ *   Same workspace as pq_gemm (pq_gemm_workspace_bytes); at M > 16 the prefill tiles are 256x256
+ *   on a ring of two stages (128x128 when a partition boundary is off a 256-column line).
  */
 size_t pq_packed_weight5_bytes(int K, int N);
 int pq_pack_weights5(const int32_t* qweight_d, const int32_t* qweight_hi_d, const int32_t* qzeros_d,
