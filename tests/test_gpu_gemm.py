@@ -95,6 +95,9 @@ def test_end_to_end_full_shapes(name):
     (33, 256, 384, (128, 128, 128)), (300, 1024, 2048, ()),
     # whole 256x256 tiles only, with 9, 1 and 3 groups (odd and short group counts)
     (512, 1152, 512, ()), (256, 128, 256, ()), (256, 384, 512, ()),
+    # row tiles in two whole bands of 4 and a last band of 1 (a whole round, then pieces), and in
+    # one whole band and a last band of 2 with three partitions (pieces only)
+    (2300, 256, 8192, ()), (1300, 512, 4096, (1024, 1024, 2048)),
 ])
 def test_gemm_ragged_shapes(M, K, N, splits):
     wl = synth.Workload("ragged", 50 + M, M, K, N, splits=splits)
