@@ -168,6 +168,29 @@ int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, in
             int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream);
 
 /*
+ * The prologue and the GEMM sharing the GEMM's workspace, so that nothing runs between them
+ * (the producer writes the consumer's operand layout directly: "2026-09-08 (late): fused TILED
+ * prologue for prefill"; the zero-point operand is the one of "2026-09-12: zero-point epilogue").
+ *
+ * pq_rotate_quant_for_gemm: pq_rotate_quant (same arguments, outputs and results) that, when
+ *   M > 16, also writes into ws_d what pq_gemm would otherwise derive from ASG and RS at the
+ *   start of each call: the activation-side zero-point operand and the group scales transposed,
+ *   computed with the same arithmetic. ws_d/ws_bytes: as for pq_gemm (at least
+ *   pq_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned); unused when M <= 16.
+ * pq_gemm_prepared: pq_gemm (same arguments and results) that reads those operands from ws_d
+ *   instead of writing them. ws_d must hold what pq_rotate_quant_for_gemm wrote for this same
+ *   (a_d, asg_d, rs_d, M, K, P), with nothing written to ws_d in between; the library cannot
+ *   check this, and any other contents give wrong outputs (never an out-of-bounds access: every
+ *   offset follows from the validated M, K and P). For M <= 16 it is pq_gemm.
+ */
+int pq_rotate_quant_for_gemm(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const void* rec_d,
+                             const uint16_t* cs_d, uint8_t* a_d, float* asg_d, float* rs_d, void* ws_d,
+                             size_t ws_bytes, pq_stream_t stream);
+int pq_gemm_prepared(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
+                     const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+                     int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream);
+
+/*
  * pq_gemm without a workspace, for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments, arithmetic,
  * kernels and results as pq_gemm, minus ws_d/ws_bytes: at M > 16 the zero-point operand and the

@@ -46,6 +46,8 @@ SIGNATURES = {
     "pq_rotate_quant": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "pq_gemm_workspace_bytes": (_SZ, [_I, _I, _I]),
     "pq_gemm": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
+    "pq_rotate_quant_for_gemm": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "pq_gemm_prepared": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
     "pq_gemm_noalloc_max_scratch_bytes": (_SZ, []),
     "pq_gemm_noalloc": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _I, _I, _P, _I64, _P]),
     "pq_rotate_quant_tok": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
@@ -252,9 +254,11 @@ def pack_weights5(qweight, qweight_hi, qzeros, qzeros_hi, scales, stream=None):
     return wpk, sz
 
 
-def _rotate_quant_common(fn, x, rec, cs, out, stream, a_dtype, tok=False):
+def _rotate_quant_common(fn, x, rec, cs, out, stream, a_dtype, tok=False, workspace=False):
     """Checks x [M, K], the records and channel scales, and caller-given outputs (codes [P, M, K],
-    scales [P, M, G] or [P, M] with tok, row-sums [P, M, G]); allocates missing outputs."""
+    scales [P, M, G] or [P, M] with tok, row-sums [P, M, G]); allocates missing outputs.
+    workspace (pq_rotate_quant_for_gemm): the GEMM workspace tensor the call also fills, checked
+    against gemm_workspace_bytes(M, N, K)."""
     import torch
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x: expected a [M, K] tensor")
@@ -266,13 +270,21 @@ def _rotate_quant_common(fn, x, rec, cs, out, stream, a_dtype, tok=False):
         A, S, R = out
         specs += [(A, "A", a_dtype, (P, M, K)), (S, "AS" if tok else "ASG", torch.float32, s_shape),
                   (R, "RS", torch.float32, (P, M, G))]
+    if workspace is not False:
+        ws_bytes = gemm_workspace_bytes(M, 0, K)
+        if workspace is None:
+            if ws_bytes:
+                raise ValueError(f"workspace: {ws_bytes} bytes needed at M={M}, K={K}")
+        else:
+            specs.append((workspace, "workspace", torch.uint8, ws_bytes))
     _validate(specs, rows=[(x, "x", torch.float16, (M, K))])
+    ws_args = () if workspace is False else (_ptr(workspace), _nbytes(workspace))
     if out is None:
         A = torch.empty((P, M, K), dtype=a_dtype, device=x.device)
         S = torch.empty(s_shape, dtype=torch.float32, device=x.device)
         R = torch.empty((P, M, G), dtype=torch.float32, device=x.device)
     _check(fn, getattr(lib(), fn)(
-        _ptr(x), x.stride(0), M, K, P, _ptr(rec), _ptr(cs), _ptr(A), _ptr(S), _ptr(R), _stream(stream)))
+        _ptr(x), x.stride(0), M, K, P, _ptr(rec), _ptr(cs), _ptr(A), _ptr(S), _ptr(R), *ws_args, _stream(stream)))
     return A, S, R
 
 
@@ -283,11 +295,21 @@ def rotate_quant(x, rec, cs, out=None, stream=None):
     return _rotate_quant_common("pq_rotate_quant", x, rec, cs, out, stream, torch.uint8)
 
 
+def rotate_quant_for_gemm(x, rec, cs, workspace, out=None, stream=None):
+    """pq_rotate_quant_for_gemm: ``rotate_quant`` that also writes, when M > 16, the prefill GEMM's
+    activation-side operands into ``workspace`` (uint8, gemm_workspace_bytes(M, N, K) bytes; None
+    allowed at M <= 16) for a following ``gemm_prepared`` on the returned (A, ASG, RS)."""
+    import torch
+    return _rotate_quant_common("pq_rotate_quant_for_gemm", x, rec, cs, out, stream, torch.uint8,
+                                workspace=workspace)
+
+
 def gemm_workspace_bytes(M, N, K):
     return int(lib().pq_gemm_workspace_bytes(M, N, K))
 
 
-def _gemm_common(fn, A, S, RS, wpk, sz, N, pb1, pb2, out, workspace, stream, *, a_dtype, tok=False, w5=False):
+def _gemm_common(fn, A, S, RS, wpk, sz, N, pb1, pb2, out, workspace, stream, *, a_dtype, tok=False, w5=False,
+                 prepared=False):
     """Checks every tensor against (P, M, K, N), allocates what is missing, calls `fn`."""
     import torch
     if not isinstance(A, torch.Tensor) or A.dim() != 3:
@@ -306,6 +328,8 @@ def _gemm_common(fn, A, S, RS, wpk, sz, N, pb1, pb2, out, workspace, stream, *, 
     ws_bytes = int(L.pq_gemm_tok_workspace_bytes(M, N, K) if tok else L.pq_gemm_workspace_bytes(M, N, K))
     if workspace is not None:
         specs.append((workspace, "workspace", torch.uint8, ws_bytes))
+    elif prepared and ws_bytes:
+        raise ValueError("workspace: gemm_prepared reads the workspace rotate_quant_for_gemm filled")
     if out is None:
         _validate(specs)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
@@ -326,6 +350,14 @@ def gemm(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, wor
     -> y bf16 [M, N] (or into ``out``, a bf16 [M, ldy >= N] view with unit column stride)."""
     import torch
     return _gemm_common("pq_gemm", A, ASG, RS, wpk, sz, N, pb1, pb2, out, workspace, stream, a_dtype=torch.uint8)
+
+
+def gemm_prepared(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, workspace=None, stream=None):
+    """pq_gemm_prepared: ``gemm`` on the workspace that ``rotate_quant_for_gemm`` filled for this same
+    (A, ASG, RS) (required when M > 16; nothing may write it in between)."""
+    import torch
+    return _gemm_common("pq_gemm_prepared", A, ASG, RS, wpk, sz, N, pb1, pb2, out, workspace, stream,
+                        a_dtype=torch.uint8, prepared=True)
 
 
 def gemm_noalloc(A, ASG, RS, wpk, sz, N, pb1=NO_BOUNDARY, pb2=NO_BOUNDARY, out=None, stream=None):

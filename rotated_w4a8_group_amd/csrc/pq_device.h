@@ -17,6 +17,20 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, (h & 0xFFFFu) << 16); }
+
+// The prefill GEMM's zero-point operand, activation side: K' = 3G values per row,
+// -[a1 | a1 | a2] with ar = asg * rs = a1 + a2 (bf16 pieces), padded with zeros to whole chunks
+// of 32. For partition p, 16-row tile mt and chunk c, 1 KiB where lane l (row 16 mt + l % 16)
+// holds the 8 bf16 at k' = 32 c + 8 (l / 16) + 0..7 (the bf16 16x16x32 operand).
+__host__ __device__ constexpr int zpe_chunks(int G) { return (3 * G + 31) / 32; }
+
+// Element index of k' of row m in that operand (MT = ceil(M / 16) row tiles, KC chunks).
+__device__ __forceinline__ size_t zpa_index(int p, int MT, int KC, int m, int kp) {
+  const int c = kp >> 5, r = kp & 31;
+  return ((static_cast<size_t>(p) * MT + (m >> 4)) * KC + c) * 512 + ((m & 15) + 16 * (r >> 3)) * 8 + (r & 7);
+}
+
 // OCP E4M3FN encode of two floats into the low 16 bits (first value in the low byte):
 // NaN -> 0, -0 -> +0, clamp to +-448, then the hardware round-to-nearest-even convert.
 // The hardware convert alone does not saturate (it yields NaN above 464) and keeps -0 and NaN;

@@ -213,11 +213,8 @@ __global__ void pack_s9_kernel(const uint32_t* __restrict__ sz, int64_t gn, floa
 // a bf16 matrix-core product with split operands: ar = a1 + a2 and zz = z1 + z2 (each piece the
 // bf16 rounding of what is left), Z ~= a1 z1 + a1 z2 + a2 z1 (relative error ~2^-16).
 // K' = 3G is laid out as [a1 | a1 | a2] x [z1 ; z2 ; z1], padded with zeros to whole chunks of 32.
-// Layout per 16-column tile t and chunk c: 1 KiB, lane l (column 16t + l%16) holds the 8 bf16
-// at k' = 32c + 8(l/16) + 0..7 — the bf16 16x16x32 B operand.
-__host__ __device__ constexpr int zpe_chunks(int G) { return (3 * G + 31) / 32; }
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, (h & 0xFFFFu) << 16); }
+// Layout per 16-column tile t and chunk c (zpe_chunks): 1 KiB, lane l (column 16t + l%16) holds
+// the 8 bf16 at k' = 32c + 8(l/16) + 0..7 — the bf16 16x16x32 B operand.
 
 template <bool kW5>
 __global__ void pack_zpe_kernel(const uint32_t* __restrict__ sz, int G, int N, u32x4* __restrict__ zpe) {
@@ -1100,10 +1097,12 @@ namespace pq {
 // the caller's.
 // ws_parts: the partition count the workspace layout is sized for (the transposed scales follow
 // the zero-point operand of that many partitions).
+// prepared: the workspace already holds those operands (pq_rotate_quant_for_gemm wrote them).
 template <bool kTok, bool kI8, bool kW5 = false>
 static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scale, const float* rs_d, int M, int K,
                        int P, const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
-                       int64_t ldy, void* ws_d, hipStream_t s, int ws_parts = PQ_MAX_PARTITIONS) {
+                       int64_t ldy, void* ws_d, hipStream_t s, int ws_parts = PQ_MAX_PARTITIONS,
+                       bool prepared = false) {
   const int G = K / PQ_GROUP;
   const u32x4* wpk = static_cast<const u32x4*>(wpk_d);
   const uint32_t* sz = reinterpret_cast<const uint32_t*>(sz_d);
@@ -1144,9 +1143,11 @@ static int gemm_launch(const char* what, const uint8_t* a_d, const float* a_scal
   u32x4* zpa = static_cast<u32x4*>(ws_d);
   float* asgt = kTok ? nullptr
                      : reinterpret_cast<float*>(static_cast<uint8_t*>(ws_d) + zpe_act_bytes(M, G, ws_parts));
-  const int64_t zt = static_cast<int64_t>(P) * ((M + 15) / 16) * zpe_chunks(G) * 64;
-  hipLaunchKernelGGL(zpe_act_kernel<kTok>, dim3(static_cast<unsigned>((zt + 255) / 256)), dim3(256), 0, s,
-                     a_scale, rs_d, M, G, P, zpa, asgt);
+  if (!prepared) {
+    const int64_t zt = static_cast<int64_t>(P) * ((M + 15) / 16) * zpe_chunks(G) * 64;
+    hipLaunchKernelGGL(zpe_act_kernel<kTok>, dim3(static_cast<unsigned>((zt + 255) / 256)), dim3(256), 0, s,
+                       a_scale, rs_d, M, G, P, zpa, asgt);
+  }
   // 16-byte output stores need a 16-byte aligned y and a row pitch of 8 elements
   const bool vec16 = aligned(y_d, 16) && ldy % 8 == 0;
   auto prefill = gemm_prefill_kernel<kTok, kI8, kW5>;
@@ -1189,6 +1190,18 @@ int pq_gemm(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, in
   if (rc != PQ_OK) return rc == 1 ? PQ_OK : rc;
   return gemm_launch<false, false>("pq_gemm", a_d, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
                             reinterpret_cast<hipStream_t>(stream));
+}
+
+int pq_gemm_prepared(const uint8_t* a_d, const float* asg_d, const float* rs_d, int M, int K, int P,
+                     const void* wpk_d, const uint16_t* sz_d, int N, int pb1, int pb2, uint16_t* y_d,
+                     int64_t ldy, void* ws_d, size_t ws_bytes, pq_stream_t stream) {
+  using namespace pq;
+  clear_error();
+  const int rc = gemm_check("pq_gemm_prepared", a_d, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy, ws_d,
+                            ws_bytes, pq_gemm_workspace_bytes(M, N, K));
+  if (rc != PQ_OK) return rc == 1 ? PQ_OK : rc;
+  return gemm_launch<false, false>("pq_gemm_prepared", a_d, asg_d, rs_d, M, K, P, wpk_d, sz_d, N, pb1, pb2, y_d, ldy,
+                                   ws_d, reinterpret_cast<hipStream_t>(stream), PQ_MAX_PARTITIONS, true);
 }
 
 int pq_gemm_tok(const uint8_t* a_d, const float* as_d, const float* rs_d, int M, int K, int P,

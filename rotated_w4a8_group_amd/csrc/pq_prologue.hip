@@ -216,16 +216,26 @@ __device__ __forceinline__ uint4 load_x8(const uint16_t* p) {
 
 // kI8: per-group int8 codes instead of e4m3 (scale amax/127, round half to even, clamp to +-127,
 // integer row-sums).
-template <bool kVec16, bool kI8>
+// kWs: also writes what the prefill GEMM derives from (asg, rs) into its workspace: the scales
+// transposed to [P][G][M] (asgt) and the zero-point operand -[a1 | a1 | a2] (zpa, zpa_index),
+// with the same arithmetic as the GEMM's own pass over ASG and RS (ar = asg * rs rounded once,
+// a1 = bf16(ar), a2 = bf16(ar - a1)), so pq_gemm_prepared can skip that pass.
+template <bool kVec16, bool kI8, bool kWs = false>
 __global__ __launch_bounds__(256) void rotate_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int K, int P,
     const uint2* __restrict__ rec, const uint16_t* __restrict__ cs, uint8_t* __restrict__ A,
-    float* __restrict__ ASG, float* __restrict__ RS, int tok, int chunks) {
+    float* __restrict__ ASG, float* __restrict__ RS, int tok, int chunks,
+    uint16_t* __restrict__ zpa = nullptr, float* __restrict__ asgt = nullptr) {
   __shared__ __align__(16) uint8_t sbuf[kProWaves][kProQuads * kProQuadBytes];
 
   const int G = K >> 7;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * kProWaves + wave;
+  // workgroups go to the 8 XCDs round-robin: give each XCD a contiguous range of workgroups, so
+  // that the units of consecutive groups of a token chunk, whose ASG/RS rows (and zero-point
+  // operand lines) share cache lines, run behind one L2
+  const int nb = gridDim.x, q8 = nb >> 3, b = blockIdx.x;
+  const int bx = b < 8 * q8 ? (b & 7) * q8 + (b >> 3) : b;
+  const int unit = bx * kProWaves + wave;
   if (unit >= chunks * G * P) return;
   const int g = unit % G;
   const int chunk = (unit / G) % chunks;
@@ -261,6 +271,12 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(
     }
   };
 
+  // kWs: this lane's fixed part of its output index (zpa_index at row 0; 32-bit: the operand
+  // has 3 M K / 128 < 2^31 elements) and the row tile stride; the scale copy's row base
+  const int zkc = zpe_chunks(G);
+  const uint32_t zrow = static_cast<uint32_t>(zkc) * 512;
+  const uint32_t zbase = kWs && c >= 1 && c < 4 ? static_cast<uint32_t>(zpa_index(p, (M + 15) >> 4, zkc, 0, (c - 1) * G + g)) : 0u;
+  const size_t abase = (static_cast<size_t>(p) * G + g) * M;
   auto run_step = [&](int mb, const uint4 (&xs)[kProQuads]) {
     // v = x * cs (exact: 11 x 11 significand bits), transposed into token-minor rows
 #pragma unroll
@@ -345,9 +361,22 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(
       const int m = mb + 4 * q + t;
       if (m < m_end) {
         *reinterpret_cast<uint2*>(A + (out_base + m) * K + g * 128 + 8 * c) = make_uint2(w[q][0], w[q][1]);
+        const float rsv = static_cast<float>(units) * 0x1p-9f;
         if (c == 0) {
           ASG[(out_base + m) * G + g] = asg[q];
-          RS[(out_base + m) * G + g] = static_cast<float>(units) * 0x1p-9f;
+          RS[(out_base + m) * G + g] = rsv;
+        }
+        if constexpr (kWs) {
+          // lane c = 0 of the token writes the transposed scale, lanes 1..3 the pieces at
+          // k' = g, G + g, 2G + g; the last group's lanes also zero the padding k' >= 3G
+          const float ar = asg[q] * rsv;
+          const uint32_t a1 = f32_to_bf16(ar), a2 = f32_to_bf16(ar - bf16_to_f32(a1));
+          const uint32_t mrow = static_cast<uint32_t>(m >> 4) * zrow + static_cast<uint32_t>(m & 15) * 8;
+          if (c == 0) asgt[abase + m] = asg[q];
+          else if (c < 4) zpa[zbase + mrow] = static_cast<uint16_t>((c == 3 ? a2 : a1) ^ 0x8000u);
+          if (g == G - 1)
+            for (int kp = 3 * G + c; kp < 32 * zkc; kp += 16)
+              zpa[zpa_index(p, (M + 15) >> 4, zkc, m, kp)] = 0;
         }
       }
     }
@@ -634,10 +663,11 @@ static int launch_status(const char* what) {
   return PQ_OK;
 }
 
-template <bool kI8>
+// ws_d (kWs): the prefill GEMM's workspace, laid out as pq_gemm_workspace_bytes sizes it.
+template <bool kI8, bool kWs = false>
 static int rotate_quant_launch(const char* what, const uint16_t* x_d, int64_t ldx, int M, int K, int P,
                                const void* rec_d, const uint16_t* cs_d, uint8_t* a_d, float* asg_d, float* rs_d,
-                               pq_stream_t stream) {
+                               pq_stream_t stream, void* ws_d = nullptr) {
   if (M < 0) return set_error(PQ_ERR_SHAPE, "%s: M=%d < 0", what, M);
   if (K <= 0 || K % PQ_GROUP || K > (1 << 24)) return set_error(PQ_ERR_SHAPE, "%s: K=%d must be a positive multiple of 128", what, K);
   if (P < 1 || P > PQ_MAX_PARTITIONS) return set_error(PQ_ERR_PARTITION, "%s: P=%d must be in 1..3", what, P);
@@ -657,11 +687,17 @@ static int rotate_quant_launch(const char* what, const uint16_t* x_d, int64_t ld
   const int64_t blocks = (units + kProWaves - 1) / kProWaves;
   if (units > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "%s: problem too large", what);
   const bool vec16 = aligned(x_d, 16) && (ldx % 8) == 0;
-  auto kern = vec16 ? rotate_quant_kernel<true, kI8> : rotate_quant_kernel<false, kI8>;
+  uint16_t* zpa = nullptr;
+  float* asgt = nullptr;
+  if constexpr (kWs) {
+    zpa = static_cast<uint16_t*>(ws_d);
+    asgt = reinterpret_cast<float*>(static_cast<uint8_t*>(ws_d) + zpe_act_bytes(M, G, PQ_MAX_PARTITIONS));
+  }
+  auto kern = vec16 ? rotate_quant_kernel<true, kI8, kWs> : rotate_quant_kernel<false, kI8, kWs>;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), x_d, ldx, M, K, P,
                      static_cast<const uint2*>(rec_d), cs_d, a_d, asg_d, rs_d, tok,
-                     static_cast<int>(chunks));
+                     static_cast<int>(chunks), zpa, asgt);
   return launch_status(what);
 }
 
@@ -675,6 +711,20 @@ int pq_rotate_quant(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const
                     pq_stream_t stream) {
   pq::clear_error();
   return pq::rotate_quant_launch<false>("pq_rotate_quant", x_d, ldx, M, K, P, rec_d, cs_d, a_d, asg_d, rs_d, stream);
+}
+
+int pq_rotate_quant_for_gemm(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const void* rec_d,
+                             const uint16_t* cs_d, uint8_t* a_d, float* asg_d, float* rs_d, void* ws_d,
+                             size_t ws_bytes, pq_stream_t stream) {
+  using namespace pq;
+  clear_error();
+  const char* what = "pq_rotate_quant_for_gemm";
+  if (M <= 16 || K <= 0 || K % PQ_GROUP)   // no prefill operands: the plain prologue (or its errors)
+    return rotate_quant_launch<false>(what, x_d, ldx, M, K, P, rec_d, cs_d, a_d, asg_d, rs_d, stream);
+  if (ws_bytes < pq_gemm_workspace_bytes(M, 0, K)) return set_error(PQ_ERR_WORKSPACE, "%s: workspace too small", what);
+  if (!ws_d) return set_error(PQ_ERR_NULL, "%s: NULL workspace", what);
+  if (!aligned(ws_d, 16)) return set_error(PQ_ERR_ALIGN, "%s: misaligned workspace", what);
+  return rotate_quant_launch<false, true>(what, x_d, ldx, M, K, P, rec_d, cs_d, a_d, asg_d, rs_d, stream, ws_d);
 }
 
 int pq_rotate_quant_i8(const uint16_t* x_d, int64_t ldx, int M, int K, int P, const void* rec_d,

@@ -142,3 +142,31 @@ def test_pack_shapes_checked():
         pq.pack_weights5(qw, qwh, qz, t((G + 1, N // 32), i32), sc)
     with pytest.raises(TypeError, match="CUDA"):
         pq.pack_weights5(qw, qwh, qz, qzh, sc)
+
+
+def test_prepared_pair_checks_the_workspace():
+    """rotate_quant_for_gemm / gemm_prepared: the workspace is required above the decode band
+    (M > 16) and checked against gemm_workspace_bytes; the other arguments as rotate_quant / gemm."""
+    Mp = 64
+    x, rec, cs = t((Mp, K), f16), t((P, 8, K // 2, 8), u8), t((P, K), f16)
+    need = pq.gemm_workspace_bytes(Mp, N, K)
+    assert need > 0
+    with pytest.raises(ValueError):
+        pq.rotate_quant_for_gemm(x, rec, cs, None)
+    with pytest.raises(ValueError):
+        pq.rotate_quant_for_gemm(x, rec, cs, t(need - 1, u8))
+    with pytest.raises(ValueError):
+        pq.rotate_quant_for_gemm(t((Mp, 200), f16), rec, cs, t(need, u8))
+    with pytest.raises(TypeError, match="CUDA"):
+        pq.rotate_quant_for_gemm(x, rec, cs, t(need, u8))
+    with pytest.raises(TypeError, match="CUDA"):     # decode band: no workspace needed
+        pq.rotate_quant_for_gemm(t((M, K), f16), rec, cs, None)
+    big = dict(A=t((P, Mp, K), u8), S=t((P, Mp, G), f32), R=t((P, Mp, G), f32))
+    with pytest.raises(ValueError):                  # a fresh workspace would hold no operands
+        call_gemm(pq.gemm_prepared, **big)
+    with pytest.raises(ValueError):
+        call_gemm(pq.gemm_prepared, workspace=t(need - 1, u8), **big)
+    with pytest.raises(ValueError):
+        call_gemm(pq.gemm_prepared, sz=t((G, N, 1), f16), workspace=t(need, u8), **big)
+    with pytest.raises(TypeError, match="CUDA"):
+        call_gemm(pq.gemm_prepared, workspace=t(need, u8), **big)
