@@ -71,6 +71,18 @@ def test_graph_per_group():
     _replays("per-group", step, [A, S, R, y])
 
 
+def test_graph_shared_workspace_pair():
+    """The prologue writes the GEMM's operands into the workspace, the GEMM reads them there."""
+    wl, x, rec, cs = _inputs(406)
+    wpk, sz = packed_weights(synth.weights(wl))
+    A, S, R, y, ws = _bufs()
+
+    def step():
+        pq.rotate_quant_for_gemm(x, rec, cs, ws, out=(A, S, R))
+        pq.gemm_prepared(A, S, R, wpk, sz, N, out=y, workspace=ws)
+    _replays("shared workspace", step, [A, S, R, y])
+
+
 def test_graph_per_token():
     wl, x, rec, cs = _inputs(402)
     wpk, sz = packed_weights(synth.weights(wl))
