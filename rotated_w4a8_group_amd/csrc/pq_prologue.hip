@@ -721,6 +721,10 @@ int pq_rotate_quant_for_gemm(const uint16_t* x_d, int64_t ldx, int M, int K, int
   const char* what = "pq_rotate_quant_for_gemm";
   if (M <= 16 || K <= 0 || K % PQ_GROUP)   // no prefill operands: the plain prologue (or its errors)
     return rotate_quant_launch<false>(what, x_d, ldx, M, K, P, rec_d, cs_d, a_d, asg_d, rs_d, stream);
+  // the prefill GEMM's own limit (32-bit activation offsets); it also keeps the zero-point
+  // operand's element indices (3 M K / 128 per partition) within 32 bits
+  if (static_cast<int64_t>(M) * K > 0x7FFFFFFF)
+    return set_error(PQ_ERR_SHAPE, "%s: M * K too large for one call (split the rows)", what);
   if (ws_bytes < pq_gemm_workspace_bytes(M, 0, K)) return set_error(PQ_ERR_WORKSPACE, "%s: workspace too small", what);
   if (!ws_d) return set_error(PQ_ERR_NULL, "%s: NULL workspace", what);
   if (!aligned(ws_d, 16)) return set_error(PQ_ERR_ALIGN, "%s: misaligned workspace", what);

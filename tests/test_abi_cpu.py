@@ -394,3 +394,41 @@ def test_records_chain_simulation_catches_a_wrong_slot(layer, shift):
     w[9] = (w[9] & ~mask) | r0
     lib[layer, :, :4] = w.view(np.uint8).reshape(-1, 4)
     assert not np.array_equal(lanes.simulate(lib, x).view(np.uint32), good.view(np.uint32))
+
+
+def _rq_ws(**kw):
+    a = dict(x=FAKE, ldx=256, M=32, K=256, P=1, rec=FAKE, cs=FAKE, A=FAKE, asg=FAKE, rs=FAKE, ws=FAKE,
+             ws_bytes=1 << 24, s=None)
+    a.update(kw)
+    return pq.lib().pq_rotate_quant_for_gemm(a["x"], a["ldx"], a["M"], a["K"], a["P"], a["rec"], a["cs"],
+                                             a["A"], a["asg"], a["rs"], a["ws"], a["ws_bytes"], a["s"])
+
+
+def test_rotate_quant_for_gemm_validation():
+    L = pq.lib()
+    assert _rq_ws(M=0, x=None, A=None, ws=None, ws_bytes=0) == 0
+    # the prologue's own checks, at a prefill M and in the decode band
+    for M in (4, 32):
+        assert _rq_ws(M=M, K=200) == -2 and _rq_ws(M=M, ldx=128) == -2 and _rq_ws(M=M, P=4) == -4
+        assert _rq_ws(M=M, x=None) == -1 and _rq_ws(M=M, x=ctypes.c_void_p(0x100002)) == -3
+    # the workspace: required above the decode band, sized as pq_gemm's, 16-byte aligned
+    need = L.pq_gemm_workspace_bytes(32, 0, 256)
+    assert need > 0
+    assert _rq_ws(ws=None) == -1
+    assert _rq_ws(ws_bytes=need - 1) == -6
+    assert _rq_ws(ws=ctypes.c_void_p(0x100008)) == -3
+    assert pq.lib().pq_last_error().decode().startswith("pq_rotate_quant_for_gemm")
+    # M * K past the prefill GEMM's 32-bit offsets fails before any launch
+    assert _rq_ws(M=300000, K=8192, ldx=8192, ws_bytes=1 << 40) == -2
+    assert "too large" in L.pq_last_error().decode()
+
+
+def test_gemm_prepared_validation():
+    name = "pq_gemm_prepared"
+    assert _gemm_variant(name, M=0, a=None, y=None) == 0
+    assert _gemm_variant(name, K=100) == -2 and _gemm_variant(name, N=120) == -2
+    assert _gemm_variant(name, P=2) == -4 and _gemm_variant(name, a=None) == -1
+    assert _gemm_variant(name, M=32, ws=None, ws_bytes=1 << 20) == -1
+    assert _gemm_variant(name, M=32, ws_bytes=pq.gemm_workspace_bytes(32, 128, 256) - 1) == -6
+    assert _gemm_variant(name, M=300000, K=8192, ws_bytes=1 << 40) == -2
+    assert pq.lib().pq_last_error().decode().startswith(name)
