@@ -65,16 +65,18 @@ const char* pq_last_error(void);
  * rec_h    out, 8 * (K/2) records of 8 bytes, layout [8][K/2]; within each (layer, group) the
  *          64 records are stored in the order the prologue's 64 lanes consume them. Record of
  *          layer r, lane l: uint32 w, f16 f1, f16 f2, where w holds the lane's pair as it
- *          computes it, u = w & 0x7F (first operand) and v = (w >> 8) & 0x7F (second), bit 15
- *          "the output kept in registers is v's", bits 16-23 the LDS hand-off row the lane reads
- *          v from (layers 1..7), bits 24-31 the row it writes its other output to (layers 0..6).
- *          The lane computes keep = f1*u + f2*v and other = g*v + d*u, with (f1, f2, g, d) =
- *          (c, s, c, -s) when u's output is kept and (-s, c, s, c) when v's is, c/s = f16
+ *          computes it, u = w & 0x7F (first operand) and v = (w >> 8) & 0x7F (second), bit 7
+ *          "v arrives negated" (t = -1; layers 1..7), bit 15 "the output kept in registers is
+ *          v's", bits 16-23 the LDS hand-off row the lane reads v from (layers 1..7), bits 24-31
+ *          the row it writes its other output to (layers 0..6). With c/s = f16
  *          round-to-nearest-even of the fp64 cos/sin of the f16 angle for the pair listed as
- *          (u, v) (listing it as (v, u) negates sin): the pair's rotation, bit for bit. Layer 0
- *          reads u and v from the quad image, layer 7 writes both outputs to it; in between each
- *          lane's kept output is the next layer's u. For P partitions call once per partition
- *          and concatenate: [P][8][K/2].
+ *          (u, v) (listing it as (v, u) negates sin), (f1, f2) = (c, t*s) when u's output is kept
+ *          and (-s, t*c) when v's is. The lane reads w = t*v and computes keep = f1*u + f2*w, the
+ *          kept output bit for bit, and hand = f1*w - f2*u, the other output times t (negated
+ *          once more when v's output is kept), which the reading lane's t accounts for. Layer 0
+ *          reads u and v from the quad image (t = 1); layer 7 keeps u's output and writes both to
+ *          the image, v's as t*hand. In between each lane's kept output is the next layer's u.
+ *          For P partitions call once per partition and concatenate: [P][8][K/2].
  * Source: section "Format" (pairs/theta) and "Design" item 3 (8-byte records).
  * Errors: PQ_ERR_NULL, PQ_ERR_SHAPE (K <= 0 or K % 128), PQ_ERR_RECORDS.
  */

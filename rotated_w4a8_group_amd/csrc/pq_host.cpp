@@ -243,18 +243,21 @@ static bool colour_regular(int n, int deg, const int* left, const int* right, in
 // the next, the two pairings form even cycles; keeping alternate channels along each cycle gives
 // every lane one output it consumes itself in the next layer (that layer's first operand) and one
 // it hands to another lane through an LDS row, chosen so that both the writes and the reads are
-// free of bank conflicts. Returns false only on an internal failure.
+// free of bank conflicts. A handed-off value may travel negated (the lane computes f1*v - f2*u
+// for either output it hands on); neg_v records that for the reader. Returns false only on an
+// internal failure.
 struct LaneRec {
   int u, v;          // the lane's pair as it computes it: u the first operand, v the second
   int rslot, wslot;  // hand-off rows read (layers 1..7) and written (layers 0..6)
   bool keep_v;       // the output kept in registers for the next layer is v's (layers 0..6)
+  bool neg_v;        // the second operand arrives negated (layers 1..7)
 };
 static bool chain_group(const int (*pi)[64], const int (*pj)[64], LaneRec (*out)[64]) {
   // layer 0: lane order and orientation from order_layer (conflict-free reads of the image)
   {
     int tail[64], head[64], lane_of[64];
     if (!order_layer(pi[0], pj[0], tail, head, lane_of)) return false;
-    for (int q = 0; q < 64; ++q) out[0][lane_of[q]] = LaneRec{tail[q], head[q], 0, 0, false};
+    for (int q = 0; q < 64; ++q) out[0][lane_of[q]] = LaneRec{tail[q], head[q], 0, 0, false, false};
   }
   for (int r = 0; r + 1 < PQ_LAYERS; ++r) {
     int nxt[128], lane_at[128];
@@ -284,7 +287,7 @@ static bool chain_group(const int (*pi)[64], const int (*pj)[64], LaneRec (*out)
     // layer r+1: lane l continues with its kept channel as the first operand
     for (int l = 0; l < 64; ++l) {
       out[r][l].keep_v = keep[l] == out[r][l].v;
-      out[r + 1][l] = LaneRec{keep[l], nxt[keep[l]], 0, 0, false};
+      out[r + 1][l] = LaneRec{keep[l], nxt[keep[l]], 0, 0, false, false};
     }
     // hand-off slots: writer lane l (8-lane block l/8) -> reader lane l2 (16-lane block l2/16);
     // slot = 16 (l2/16) + rho with rho distinct in each reader block (reads: rows distinct mod 16)
@@ -302,6 +305,9 @@ static bool chain_group(const int (*pi)[64], const int (*pj)[64], LaneRec (*out)
       const int slot = 16 * (reader[l] / 16) + col[l] + 8 * (hr[l] & 1);
       out[r][l].wslot = slot;
       out[r + 1][reader[l]].rslot = slot;
+      // the handed output carries the writer's operand sign, flipped once more when v's output
+      // is the one kept (see pq_build_records)
+      out[r + 1][reader[l]].neg_v = out[r][l].neg_v != out[r][l].keep_v;
     }
   }
   return true;
@@ -357,12 +363,17 @@ int pq_build_records(const int16_t* pairs_h, const uint16_t* theta_h, int K, voi
         // (c, s) of the pair listed as (u, v): listing it as (j, i) negates sin
         const uint16_t c = c16[r][q];
         const uint16_t sn = (pi[r][q] == e.u) ? s16[r][q] : static_cast<uint16_t>(s16[r][q] ^ 0x8000);
-        // kept output u: keep = c u + s v, other = c v - s u  -> (f1, f2) = (c, s)
-        // kept output v: keep = -s u + c v, other = s v + c u -> (f1, f2) = (-s, c)
+        // The lane reads w = t v (t = -1 when neg_v) and computes keep = f1 u + f2 w and
+        // hand = f1 w - f2 u:
+        //   kept output u: (f1, f2) = (c, t s): keep = c u + s v,  hand = t (c v - s u)
+        //   kept output v: (f1, f2) = (-s, t c): keep = c v - s u, hand = -t (c u + s v)
+        // so a handed value is the other output times t, negated again when v's is kept. The last
+        // layer keeps u's output and writes t * hand, v's output, to the image.
         const bool kv = (r + 1 < PQ_LAYERS) && e.keep_v;
+        const uint16_t t = e.neg_v ? 0x8000 : 0;
         const uint16_t f1 = kv ? static_cast<uint16_t>(sn ^ 0x8000) : c;
-        const uint16_t f2 = kv ? c : sn;
-        const uint32_t w = static_cast<uint32_t>(e.u) | (static_cast<uint32_t>(e.v) << 8) |
+        const uint16_t f2 = static_cast<uint16_t>((kv ? c : sn) ^ t);
+        const uint32_t w = static_cast<uint32_t>(e.u) | (e.neg_v ? 0x80u : 0u) | (static_cast<uint32_t>(e.v) << 8) |
                            (kv ? 0x8000u : 0u) | (static_cast<uint32_t>(r > 0 ? e.rslot : 0) << 16) |
                            (static_cast<uint32_t>(r + 1 < PQ_LAYERS ? e.wslot : 0) << 24);
         uint8_t* dst = out.data() + (static_cast<size_t>(r) * half + g * 64 + l) * 8;

@@ -48,16 +48,24 @@ __device__ __forceinline__ uint32_t lds_row_bytes(uint32_t ch) { return (ch + (c
 // image; afterwards a lane keeps one output of each layer in registers (the next layer's first
 // operand) and passes the other through a hand-off row of LDS to the lane that needs it, so
 // layers 1..6 read and write one row per quad instead of two; layer 7 writes both outputs to the
-// image. Per token: keep = f1*u + f2*v, other = g*v + d*u, every product and sum rounding to
-// binary32 (this TU has contraction off) -- the pair's rotation, with the two outputs in either
-// order.
+// image. Per token, with u the first operand and w the second: keep = f1*u + f2*w and
+// hand = f1*w - f2*u, every product and sum rounding to binary32 (this TU has contraction off).
+// The records fold into f1 and f2 which output is kept and whether w arrives negated, so keep is
+// the pair's rotated value bit for bit and hand is the other one, possibly negated; in layer 7
+// the lane negates (f1, f2) for hand when the record's bit 7 says w arrived negated, which makes
+// it the rotated value too. A negated hand-off can differ from the exact negation only in the
+// sign of an exact zero, which no code, scale or row-sum sees.
 struct RotRec {
   uint32_t u0, v0;                 // layer 0: image rows of u and v (bytes)
   uint32_t rd[PQ_LAYERS];          // layers 1..7: hand-off row read (bytes)
   uint32_t wr[PQ_LAYERS];          // layers 0..6: hand-off row written (bytes)
   uint32_t u7, v7;                 // layer 7: image rows of u and v (bytes)
-  float f1[PQ_LAYERS], f2[PQ_LAYERS], g[PQ_LAYERS], d[PQ_LAYERS];
+  float f1[PQ_LAYERS], f2[PQ_LAYERS];
+  float g7, d7;                    // layer 7: (f1, f2) for v's output
 };
+
+// Layer 7's sign for v's output: bit 7 of the record word moved to the float sign bit.
+__device__ __forceinline__ uint32_t last_layer_sign(uint32_t x) { return (x << 24) & 0x80000000u; }
 
 __device__ __forceinline__ void rot_decode(const uint2 (&q)[PQ_LAYERS], RotRec& R) {
   R.u0 = lds_row_bytes(q[0].x & 0x7Fu);
@@ -68,12 +76,12 @@ __device__ __forceinline__ void rot_decode(const uint2 (&q)[PQ_LAYERS], RotRec& 
   for (int r = 0; r < PQ_LAYERS; ++r) {
     R.rd[r] = ((q[r].x >> 16) & 0xFFu) << 4;
     R.wr[r] = (q[r].x >> 24) << 4;
-    const uint32_t keep_v = (q[r].x >> 15) & 1u;   // v's output kept: (g, d) = (-f1, f2), else (f1, -f2)
     R.f1[r] = f16_to_f32(q[r].y);
     R.f2[r] = f16_to_f32(q[r].y >> 16);
-    R.g[r] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, R.f1[r]) ^ (keep_v << 31));
-    R.d[r] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, R.f2[r]) ^ ((keep_v ^ 1u) << 31));
   }
+  const uint32_t m = last_layer_sign(q[PQ_LAYERS - 1].x);
+  R.g7 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, R.f1[PQ_LAYERS - 1]) ^ m);
+  R.d7 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, R.f2[PQ_LAYERS - 1]) ^ m);
 }
 
 // NQ quad images at buf + q * QB.
@@ -92,12 +100,13 @@ __device__ __forceinline__ void rot_layers(uint8_t* buf, const RotRec& R) {
     for (int q = 0; q < NQ; ++q) {
       const float av[4] = {a[q].x, a[q].y, a[q].z, a[q].w}, bv[4] = {b[q].x, b[q].y, b[q].z, b[q].w};
       float kp[4], ot[4];
+      const float gg = r + 1 < PQ_LAYERS ? R.f1[r] : R.g7, dd = r + 1 < PQ_LAYERS ? R.f2[r] : R.d7;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float x1 = R.f1[r] * av[k], x2 = R.f2[r] * bv[k];
-        const float y1 = R.g[r] * bv[k], y2 = R.d[r] * av[k];
+        const float y1 = gg * bv[k], y2 = dd * av[k];
         kp[k] = x1 + x2;
-        ot[k] = y1 + y2;
+        ot[k] = y1 - y2;
       }
       if (r + 1 < PQ_LAYERS) {
         reg[q] = make_float4(kp[0], kp[1], kp[2], kp[3]);
@@ -119,10 +128,10 @@ __device__ __forceinline__ void rot_layers_q(uint8_t* buf, const uint2 (&q)[PQ_L
 #pragma unroll
   for (int r = 0; r < PQ_LAYERS; ++r) {
     const uint32_t x = q[r].x;
-    const uint32_t keep_v = (x >> 15) & 1u;
     const float f1 = f16_to_f32(q[r].y), f2 = f16_to_f32(q[r].y >> 16);
-    const float gg = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f1) ^ (keep_v << 31));
-    const float dd = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f2) ^ ((keep_v ^ 1u) << 31));
+    const uint32_t m = r + 1 < PQ_LAYERS ? 0u : last_layer_sign(x);
+    const float gg = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f1) ^ m);
+    const float dd = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f2) ^ m);
     const uint32_t ra = lds_row_bytes(x & 0x7Fu), rb = lds_row_bytes((x >> 8) & 0x7Fu);
     float4 a[NQ], b[NQ];
 #pragma unroll
@@ -139,7 +148,7 @@ __device__ __forceinline__ void rot_layers_q(uint8_t* buf, const uint2 (&q)[PQ_L
         const float x1 = f1 * av[k], x2 = f2 * bv[k];
         const float y1 = gg * bv[k], y2 = dd * av[k];
         kp[k] = x1 + x2;
-        ot[k] = y1 + y2;
+        ot[k] = y1 - y2;
       }
       if (r + 1 < PQ_LAYERS) {
         reg[qd] = make_float4(kp[0], kp[1], kp[2], kp[3]);

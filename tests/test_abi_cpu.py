@@ -396,6 +396,28 @@ def test_records_chain_simulation_catches_a_wrong_slot(layer, shift):
     assert not np.array_equal(lanes.simulate(lib, x).view(np.uint32), good.view(np.uint32))
 
 
+@pytest.mark.parametrize("layer,field", [(7, "neg_v"), (3, "f2"), (0, "f1")])
+def test_records_chain_simulation_catches_a_wrong_sign(layer, field):
+    """The signs folded into the records matter: the last layer's "v arrives negated" bit, or one
+    coefficient's sign in a middle layer (where the hand-off sign is folded into f2) or in the
+    first, flipped for one lane, changes the result; and such a flip in a middle layer is also
+    seen by the decoding of the records' rotations."""
+    wl = synth.WORKLOADS["tiny"]
+    pl, tl, cl = synth.rotations(wl)
+    lib = pq.build_records(pl[0], tl[0]).copy()
+    x = synth.activations(wl).astype(np.float32)
+    good = lanes.simulate(lib, x)
+    lane = 5
+    if field == "neg_v":
+        lib[layer, lane, 0] ^= 0x80
+    else:
+        lib[layer, lane, 5 if field == "f1" else 7] ^= 0x80       # the f16's sign bit
+    assert not np.array_equal(lanes.simulate(lib, x).view(np.uint32), good.view(np.uint32))
+    if field != "neg_v":
+        ref = orec.build(pl[0][:, :128], tl[0][:, :64])
+        assert lanes.canonical(lanes.decode(lib), layer, slice(0, 64)) != _ref_rotations(ref, layer, slice(0, 64))
+
+
 def _rq_ws(**kw):
     a = dict(x=FAKE, ldx=256, M=32, K=256, P=1, rec=FAKE, cs=FAKE, A=FAKE, asg=FAKE, rs=FAKE, ws=FAKE,
              ws_bytes=1 << 24, s=None)
