@@ -42,6 +42,31 @@ constexpr int kProUnits = 16384;             // aim for about this many wave uni
 
 __device__ __forceinline__ uint32_t lds_row_bytes(uint32_t ch) { return (ch + (ch >> 3)) << 4; }
 
+// Products with binary16 operands read from a half of a 32-bit word (HI selects the upper one),
+// as single v_fma_mix_f32 instructions with a -0 addend: the fused operation rounds the exact
+// product once, and adding -0 changes no value (-0 + -0 = -0), so each equals the binary32
+// multiply of the converted operands bit for bit, without the conversions.
+//   mul_hf<HI>(h2, a)       = fl32(f32(half HI of h2) * a)
+//   mul_hh<HI>(a2, b2)      = fl32(f32(half HI of a2) * f32(half HI of b2))
+template <bool HI>
+__device__ __forceinline__ float mul_hf(uint32_t h2, float a) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(a), "s"(-0.0f));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(a), "s"(-0.0f));
+  return r;
+}
+template <bool HI>
+__device__ __forceinline__ float mul_hh(uint32_t a2, uint32_t b2) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "=v"(r) : "v"(a2), "v"(b2), "s"(-0.0f));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,1,0]" : "=v"(r) : "v"(a2), "v"(b2), "s"(-0.0f));
+  return r;
+}
+
 // The 8 rotation layers of one token-group, driven by the lane's records (layout in pq.h): on
 // entry every channel ch of a quad sits in the 16-byte image row lds_row(ch) (4 tokens), on exit
 // the rotated channels are back in those rows. Layer 0 reads both of the lane's channels from the
@@ -213,6 +238,11 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
 __device__ __forceinline__ float half_lo(uint32_t w) { return f16_to_f32(w); }
 __device__ __forceinline__ float half_hi(uint32_t w) { return f16_to_f32(w >> 16); }
 
+// Buffer resource for bytes [base, base + bytes) (raw, no swizzle; gfx9 data format word).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
 template <bool kVec16>
 __device__ __forceinline__ uint4 load_x8(const uint16_t* p) {
   if constexpr (kVec16) {
@@ -264,7 +294,13 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(
     rot_decode(q, R);
   }
   const uint32_t* csp = reinterpret_cast<const uint32_t*>(cs + static_cast<size_t>(p) * K + g * 128 + 8 * c);
-  const uint32_t cw[4] = {csp[0], csp[1], csp[2], csp[3]};
+  float csf[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = csp[i];
+    csf[2 * i] = half_lo(w);
+    csf[2 * i + 1] = half_hi(w);
+  }
 
   uint8_t* const buf = sbuf[wave];
   // this lane's scalar slot in a quad: channel 8c+j of token t at row 9c+j, dword t
@@ -293,8 +329,8 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(
       const uint32_t xw[4] = {xs[q].x, xs[q].y, xs[q].z, xs[q].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<float*>(slot + q * kProQuadBytes + (2 * i) * 16) = half_lo(xw[i]) * half_lo(cw[i]);
-        *reinterpret_cast<float*>(slot + q * kProQuadBytes + (2 * i + 1) * 16) = half_hi(xw[i]) * half_hi(cw[i]);
+        *reinterpret_cast<float*>(slot + q * kProQuadBytes + (2 * i) * 16) = mul_hf<false>(xw[i], csf[2 * i]);
+        *reinterpret_cast<float*>(slot + q * kProQuadBytes + (2 * i + 1) * 16) = mul_hf<true>(xw[i], csf[2 * i + 1]);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -431,8 +467,10 @@ __global__ __launch_bounds__(64 * kTokWaves) void rotate_quant_tok_kernel(
   uint8_t* const buf = qbuf[wave];
   uint8_t* const slot = buf + (9 * c) * 16 + 4 * t;
   const uint16_t* const xrow = x + static_cast<size_t>(mld) * ldx + 8 * c;
-  const uint16_t* const csp = cs + static_cast<size_t>(p) * K + 8 * c;
-  const uint2* const recp = rec + static_cast<size_t>(p) * PQ_LAYERS * half + lane;
+  // records and channel scales through buffer loads: the lane's offset is fixed, the layer and
+  // group part of the address is wave-uniform and goes in the scalar offset
+  const __amdgpu_buffer_rsrc_t rec_rs = make_rsrc(rec + static_cast<size_t>(p) * PQ_LAYERS * half, 64 * half);
+  const __amdgpu_buffer_rsrc_t cs_rs = make_rsrc(cs + static_cast<size_t>(p) * K, 2 * K);
 
   float park[NPG][8];
   float tmax = 0.0f;
@@ -442,15 +480,18 @@ __global__ __launch_bounds__(64 * kTokWaves) void rotate_quant_tok_kernel(
     if (g < G) {
       uint2 q[PQ_LAYERS];
 #pragma unroll
-      for (int r = 0; r < PQ_LAYERS; ++r) q[r] = recp[static_cast<size_t>(r) * half + g * 64];
-      const uint32_t* cw = reinterpret_cast<const uint32_t*>(csp + g * 128);
-      const uint32_t cs4[4] = {cw[0], cw[1], cw[2], cw[3]};
+      for (int r = 0; r < PQ_LAYERS; ++r) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rec_rs, 8 * lane, 8 * (r * half + g * 64), 0);
+        q[r] = make_uint2(v[0], v[1]);
+      }
+      const auto cv = __builtin_amdgcn_raw_buffer_load_b128(cs_rs, 16 * c, 256 * g, 0);
+      const uint32_t cs4[4] = {cv[0], cv[1], cv[2], cv[3]};
       const uint4 xs = load_x8<kVec16>(xrow + g * 128);
       const uint32_t xw[4] = {xs.x, xs.y, xs.z, xs.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<float*>(slot + (2 * i) * 16) = half_lo(xw[i]) * half_lo(cs4[i]);
-        *reinterpret_cast<float*>(slot + (2 * i + 1) * 16) = half_hi(xw[i]) * half_hi(cs4[i]);
+        *reinterpret_cast<float*>(slot + (2 * i) * 16) = mul_hh<false>(xw[i], cs4[i]);
+        *reinterpret_cast<float*>(slot + (2 * i + 1) * 16) = mul_hh<true>(xw[i], cs4[i]);
       }
       __builtin_amdgcn_wave_barrier();
       rot_layers_q<1, kProQuadBytes>(buf, q);
@@ -612,8 +653,8 @@ __global__ __launch_bounds__(64 * kTokWaves) void add_rms_rotate_quant_kernel(
       const uint32_t cs4[4] = {cw[0], cw[1], cw[2], cw[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<float*>(slot + (2 * i) * 16) = half_lo(hp[j][i]) * half_lo(cs4[i]);
-        *reinterpret_cast<float*>(slot + (2 * i + 1) * 16) = half_hi(hp[j][i]) * half_hi(cs4[i]);
+        *reinterpret_cast<float*>(slot + (2 * i) * 16) = mul_hh<false>(hp[j][i], cs4[i]);
+        *reinterpret_cast<float*>(slot + (2 * i + 1) * 16) = mul_hh<true>(hp[j][i], cs4[i]);
       }
       __builtin_amdgcn_wave_barrier();
       rot_layers_q<1, kProQuadBytes>(buf, q);
@@ -709,7 +750,6 @@ static int rotate_quant_launch(const char* what, const uint16_t* x_d, int64_t ld
                      static_cast<int>(chunks), zpa, asgt);
   return launch_status(what);
 }
-
 
 }  // namespace pq
 
