@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--ceilings-only", action="store_true",
                     help="only measure the HBM read and fp8 matrix-core ceilings and print them")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured ceilings")
+    ap.add_argument("--prologue-only", metavar="WORKLOAD",
+                    help="only run one synthetic workload's prologues, 5 calls each of the per-group, "
+                         "per-token and GEMM-workspace-filling forms (for counter passes)")
     ap.add_argument("--gemm-only", metavar="WORKLOAD",
                     help="only run one synthetic workload (synth.WORKLOADS name): its prologue once, then "
                          "5 GEMM calls (for counter passes that must see one shape)")
@@ -196,6 +199,9 @@ def main():
 
     if args.gemm_only:
         gemm_only(args.gemm_only, torch, np)
+        return
+    if args.prologue_only:
+        prologue_only(args.prologue_only, torch, np)
         return
     ceilings = None if args.no_ceilings else measure_ceilings(torch, np)
 
@@ -519,6 +525,32 @@ def gemm_only(name, torch, np, calls=5):
     torch.cuda.synchronize()
     print(json.dumps({"gemm_only": name, "M": M, "K": K, "N": N, "partitions": P, "calls": calls,
                       "algorithmic_bytes": gemm_bytes(M, K, N, P)}), flush=True)
+
+
+def prologue_only(name, torch, np, calls=5):
+    """One workload's prologues, `calls` launches each of pq_rotate_quant, pq_rotate_quant_tok and
+    pq_rotate_quant_for_gemm, nothing else (for rocprofv3 counter passes over the prologue kernels)."""
+    import rotated_w4a8_group_amd as pq
+    import synth
+    wl = synth.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    M, K, N = wl.M, wl.K, wl.N
+    pl, tl, cl = synth.rotations(wl)
+    rec = torch.from_numpy(np.stack([pq.build_records(p, t) for p, t in zip(pl, tl)])).to(dev)
+    cs = torch.from_numpy(np.stack(cl)).to(dev)
+    x = torch.from_numpy(synth.activations(wl)).to(dev)
+    out = pq.rotate_quant(x, rec, cs)
+    out_tok = pq.rotate_quant_tok(x, rec, cs)
+    ws = torch.empty(max(1, pq.gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dev)
+    for _ in range(calls):
+        pq.rotate_quant(x, rec, cs, out=out)
+    for _ in range(calls):
+        pq.rotate_quant_tok(x, rec, cs, out=out_tok)
+    for _ in range(calls):
+        pq.rotate_quant_for_gemm(x, rec, cs, ws, out=out)
+    torch.cuda.synchronize()
+    print(json.dumps({"prologue_only": name, "M": M, "K": K, "partitions": wl.P, "calls": calls,
+                      "algorithmic_bytes": prologue_bytes(M, K, wl.P)}), flush=True)
 
 
 def config_measurement(wl, pq, torch, np, dev, copies, tok=False, i8=False, w5=False):

@@ -157,7 +157,8 @@ def main(argv=None):
     t.add_argument("--command", action="append", default=[])
     c = sub.add_parser("counters")
     c.add_argument("db")
-    c.add_argument("--kernels", required=True)
+    c.add_argument("--kernels", required=True, help="kernel name patterns, separated by ',' (or by ';' "
+                                                    "when a pattern holds a comma)")
     c.add_argument("--cus", type=int, default=256)
     c.add_argument("--xcds", type=int, default=8)
     c.add_argument("--title", default="")
@@ -166,7 +167,8 @@ def main(argv=None):
     if a.cmd == "summary":
         sys.stdout.write(summary(a.db, a.title, a.command))
     elif a.cmd == "counters":
-        sys.stdout.write(counters_table(a.db, a.kernels.split(","), a.cus, a.xcds, a.title, a.command))
+        pats = a.kernels.split(";" if ";" in a.kernels else ",")
+        sys.stdout.write(counters_table(a.db, pats, a.cus, a.xcds, a.title, a.command))
     else:
         rec = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.kernels.split(","), a.source,
                       a.copy_bytes, a.algorithmic_bytes, a.command)
