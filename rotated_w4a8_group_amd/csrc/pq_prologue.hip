@@ -187,9 +187,11 @@ __device__ __forceinline__ void rot_layers_q(uint8_t* buf, const uint2 (&q)[PQ_L
   }
 }
 
+// Lane permutation within a 16-lane row (every lane has a source: the bound_ctrl setting never
+// applies), in a form the compiler folds into the consuming max or add.
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
 // Reductions over the 16 lanes of a DPP row: swap within pairs, within quads, mirror the
@@ -231,7 +233,9 @@ __device__ __forceinline__ int code_units(uint32_t w0, uint32_t w1) {
 }
 
 __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first convert writes bytes 0-1 and keeps the rest of its "old" operand, which the second
+  // convert overwrites (bytes 2-3): any register serves as that operand
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
 }
 
