@@ -10,11 +10,18 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu)));
 }
 
-// fp32 -> bf16 bit pattern, round to nearest even (NaN kept quiet).
+// fp32 -> bf16 bit pattern, round to nearest even, with gfx950's convert instruction. Its result
+// equals the integer rounding (u + 0x7FFF + bit 16 of u) >> 16, a NaN becoming the quiet NaN
+// (u >> 16) | 0x40, bit for bit on every one of the 2^32 inputs (compared exhaustively on the
+// device): one instruction where the integer form took a compare, a branch and three to four more.
+typedef float pq_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 pq_bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// Two at once: lo in bits 0-15, hi in bits 16-31 (one packed convert).
+__device__ __forceinline__ uint32_t bf16x2_rn(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(pq_f32x2{lo, hi}, pq_bf16x2));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, (h & 0xFFFFu) << 16); }

@@ -275,6 +275,9 @@ __global__ void zpe_act_kernel(const float* __restrict__ ASG, const float* __res
   uint32_t h[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
+    // ar = fl32(asg rs) and a2 = bf16(ar - a1) round separately, as where the prologue writes
+    // these operands: the multiply must not fuse into the subtraction
+#pragma clang fp contract(off)
     uint32_t v = 0;
     if (piece[e] >= 0) {
       const float ar = kTok ? rv[e] : av[e] * rv[e];
@@ -504,7 +507,7 @@ __device__ __forceinline__ void decode_body(
       s0 += sred[(w * 16 + m) * 16 * NT + c];
       s1 += sred[(w * 16 + m) * 16 * NT + c + 1];
     }
-    *reinterpret_cast<uint32_t*>(y + static_cast<size_t>(m) * ldy + n0 + c) = f32_to_bf16(s0) | (f32_to_bf16(s1) << 16);
+    *reinterpret_cast<uint32_t*>(y + static_cast<size_t>(m) * ldy + n0 + c) = bf16x2_rn(s0, s1);
   }
 }
 
@@ -889,7 +892,7 @@ __device__ __forceinline__ void prefill_tile(
       v4f v = acc[mf][nf];
       if constexpr (kTok) v *= a;
       *reinterpret_cast<uint2*>(ot + (wm * MF * 16 + 16 * mf + (lane & 15)) * TL::kOutStride + wn * NF * 16 + 16 * nf + 4 * kq) =
-          make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
+          make_uint2(bf16x2_rn(v[0], v[1]), bf16x2_rn(v[2], v[3]));
     }
   }
   __syncthreads();
