@@ -321,9 +321,15 @@ int pq_add_rms_rotate_quant(const uint16_t* x_d, int64_t ldx, const uint16_t* re
  * tests can check it exhaustively.
  *  pq_e4m3_encode: codes_d[i] = E(q_d[i]) with the prologue's encoder (n >= 0).
  *  pq_recip_f32:   y_d[i] = 1 / x_d[i] with the prologue's reciprocal.
+ *  pq_bf16_round:  out_d[i] = the bf16 bits of x_d[i] with the rounding of the GEMM outputs and the
+ *                  zero-point operands (round to nearest even; a NaN becomes a quiet NaN with its
+ *                  sign and top payload bits), pairs through the epilogues' packed convert.
+ * Arguments: device arrays of n elements (n >= 0; 4-byte aligned floats, 2-byte aligned outputs).
+ * Errors: PQ_ERR_SHAPE (n < 0 or too large), PQ_ERR_NULL, PQ_ERR_ALIGN, PQ_ERR_DEVICE.
  */
 int pq_e4m3_encode(const float* q_d, uint8_t* codes_d, int64_t n, pq_stream_t stream);
 int pq_recip_f32(const float* x_d, float* y_d, int64_t n, pq_stream_t stream);
+int pq_bf16_round(const float* x_d, uint16_t* out_d, int64_t n, pq_stream_t stream);
 
 #ifdef __cplusplus
 }

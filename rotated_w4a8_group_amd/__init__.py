@@ -62,6 +62,7 @@ SIGNATURES = {
                                      _P, _P, _P, _P, _P]),
     "pq_e4m3_encode": (_I, [_P, _P, _I64, _P]),
     "pq_recip_f32": (_I, [_P, _P, _I64, _P]),
+    "pq_bf16_round": (_I, [_P, _P, _I64, _P]),
 }
 
 
@@ -473,4 +474,13 @@ def recip_f32(x, stream=None):
     _need(x, torch.float32, "x")
     out = torch.empty_like(x)
     _check("pq_recip_f32", lib().pq_recip_f32(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    return out
+
+
+def bf16_round(x, stream=None):
+    """float32 CUDA tensor -> int16 tensor of bf16 bit patterns with the GEMM's device rounding."""
+    import torch
+    _need(x, torch.float32, "x")
+    out = torch.empty(x.shape, dtype=torch.int16, device=x.device)
+    _check("pq_bf16_round", lib().pq_bf16_round(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
     return out

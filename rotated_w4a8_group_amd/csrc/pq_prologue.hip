@@ -696,6 +696,19 @@ __global__ __launch_bounds__(64 * kTokWaves) void add_rms_rotate_quant_kernel(
   }
 }
 
+// Verification hook: out[i] = bf16 bits of x[i] with the rounding of the GEMM outputs, two elements per thread
+// through the packed convert of the epilogues, a last odd element through the single one.
+__global__ void bf16_round_kernel(const float* __restrict__ x, uint16_t* __restrict__ out, int64_t n) {
+  const int64_t i = 2 * (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
+  if (i + 1 < n) {
+    const uint32_t w = bf16x2_rn(x[i], x[i + 1]);
+    out[i] = static_cast<uint16_t>(w);
+    out[i + 1] = static_cast<uint16_t>(w >> 16);
+  } else if (i < n) {
+    out[i] = static_cast<uint16_t>(f32_to_bf16(x[i]));
+  }
+}
+
 __global__ void e4m3_encode_kernel(const float* __restrict__ q, uint8_t* __restrict__ out, int64_t n) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 2;
   if (i + 1 < n) {
@@ -908,6 +921,21 @@ int pq_recip_f32(const float* x_d, float* y_d, int64_t n, pq_stream_t stream) {
   hipLaunchKernelGGL(recip_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), x_d, y_d, n);
   return launch_status("pq_recip_f32");
+}
+
+int pq_bf16_round(const float* x_d, uint16_t* out_d, int64_t n, pq_stream_t stream) {
+  using namespace pq;
+  clear_error();
+  if (n < 0) return set_error(PQ_ERR_SHAPE, "pq_bf16_round: n < 0");
+  if (n == 0) return PQ_OK;
+  if (!x_d || !out_d) return set_error(PQ_ERR_NULL, "pq_bf16_round: NULL pointer");
+  if (!aligned(x_d, 4) || !aligned(out_d, 2)) return set_error(PQ_ERR_ALIGN, "pq_bf16_round: misaligned pointer");
+  const int64_t threads = (n + 1) / 2;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return set_error(PQ_ERR_SHAPE, "pq_bf16_round: n too large");
+  hipLaunchKernelGGL(bf16_round_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), x_d, out_d, n);
+  return launch_status("pq_bf16_round");
 }
 
 }  // extern "C"

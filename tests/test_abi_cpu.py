@@ -315,6 +315,9 @@ def test_hooks_validation():
     assert L.pq_e4m3_encode(FAKE, FAKE, -1, None) == -2
     assert L.pq_e4m3_encode(None, None, 0, None) == 0
     assert L.pq_recip_f32(None, FAKE, 5, None) == -1
+    assert L.pq_bf16_round(FAKE, FAKE, -1, None) == -2
+    assert L.pq_bf16_round(None, None, 0, None) == 0
+    assert L.pq_bf16_round(FAKE, None, 3, None) == -1
 
 
 def _proj(seed, K=256, ncols=128):

@@ -156,3 +156,23 @@ def test_packed_sz_definition():
     assert np.array_equal(sz[..., 0].view(np.uint16), w.scales.view(np.uint16))
     want = (w.scales.astype(np.float32) * (w.zp.astype(np.float32) - 8)).astype(np.float16)
     assert np.array_equal(sz[..., 1].view(np.uint16), want.view(np.uint16))
+
+
+def test_device_bf16_rounding_exhaustive():
+    """The bf16 rounding of the GEMM outputs and zero-point operands (pq_bf16_round: pairs through
+    the epilogues' packed convert, an odd last element through the single one) on all 2^32 fp32
+    bit patterns: round to nearest even as torch's float32 -> bfloat16 conversion does it for every
+    non-NaN input, and a NaN kept quiet with its sign and top payload bits ((u >> 16) | 0x40)."""
+    chunk = 1 << 28
+    bad = 0
+    for c in range(1 << 4):
+        lo = -(1 << 31) + c * chunk
+        bits = torch.arange(lo, lo + chunk + (1 if c == 0 else 0), dtype=torch.int32, device="cuda")  # odd length once
+        got = pq.bf16_round(bits.view(torch.float32)).to(torch.int32) & 0xFFFF
+        want = bits.view(torch.float32).to(torch.bfloat16).view(torch.int16).to(torch.int32) & 0xFFFF
+        nan = (bits & 0x7FFFFFFF) > 0x7F800000
+        want = torch.where(nan, ((bits >> 16) & 0xFFFF) | 0x40, want)
+        bad += int((got != want).sum())
+        del bits, got, want, nan
+    print(f"[bf16] mismatches over 2^32 inputs: {bad}", flush=True)
+    assert bad == 0
